@@ -1,0 +1,10 @@
+"""CPU oracle (test infrastructure only; see oracle/attention.py)."""
+from .attention import (  # noqa: F401
+    attention_bruteforce,
+    attention_fp64,
+    attention_online_fp64,
+    attention_rows_fp64,
+    attention_weights_fp64,
+    score_matrix_bytes,
+    score_matrix_gb,
+)

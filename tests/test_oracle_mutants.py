@@ -1,0 +1,97 @@
+"""Plant plausible mistakes in the oracle's steps (on the CPU) and check that
+each one makes at least one pin fail. This shows the pins constrain every step
+of the definition: the score product, the masks, the softmax, the weighted sum
+and the log-sum-exp."""
+import numpy as np
+import pytest
+
+import oracle.attention as A
+from oracle_pins import PINS
+
+NEG_INF = -np.inf
+
+
+def _causal_off_by_one(S, q_pos, causal, kpm_row):
+    if causal:
+        S[np.arange(S.shape[1])[None, :] >= q_pos[:, None]] = NEG_INF
+    if kpm_row is not None:
+        S[:, np.asarray(kpm_row) != 0] = NEG_INF
+    return S
+
+
+def _padding_ignored(S, q_pos, causal, kpm_row):
+    if causal:
+        S[np.arange(S.shape[1])[None, :] > q_pos[:, None]] = NEG_INF
+    return S
+
+
+def _causal_bottom_right(S, q_pos, causal, kpm_row):
+    if causal:
+        off = S.shape[1] - (q_pos.max() + 1 if q_pos.size else 0)
+        S[np.arange(S.shape[1])[None, :] > q_pos[:, None] + off] = NEG_INF
+    if kpm_row is not None:
+        S[:, np.asarray(kpm_row) != 0] = NEG_INF
+    return S
+
+
+def _no_max_shift(S):
+    with np.errstate(over="ignore", invalid="ignore"):
+        E = np.exp(S)
+        L = E.sum(axis=1)
+        P = np.where(L[:, None] > 0, E / np.where(L > 0, L, 1)[:, None], 0.0)
+    M = np.zeros(S.shape[0])
+    M[~(L > 0)] = NEG_INF
+    return P, M, L
+
+
+def _sum_drops_last_key(S):
+    P, M, L = ORIG["_softmax_rows"](S)
+    if S.shape[1] > 1:
+        Ms = np.where(np.isneginf(M), 0.0, M)
+        E = np.exp(S - Ms[:, None])
+        L = E[:, :-1].sum(axis=1)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            P = np.where(L[:, None] > 0, E / np.where(L > 0, L, 1)[:, None], 0.0)
+    return P, M, L
+
+
+def _max_not_subtracted_back(S):
+    P, M, L = ORIG["_softmax_rows"](S)
+    return P, np.zeros_like(M) * np.where(np.isneginf(M), np.nan, 1.0), L
+
+
+ORIG = {n: getattr(A, n) for n in ("_scores", "_apply_masks", "_softmax_rows",
+                                    "_weighted_values", "_log_sum_exp")}
+
+MUTANTS = {
+    "score_without_scale": ("_scores", lambda q, k, s: q @ k.T),
+    "score_scale_squared": ("_scores", lambda q, k, s: np.float64(s) ** 2 * (q @ k.T)),
+    "score_drops_last_feature": ("_scores", lambda q, k, s: np.float64(s) * (q[:, :-1] @ k[:, :-1].T)),
+    "score_operands_swapped": ("_scores", lambda q, k, s: np.float64(s) * (k @ q.T)),
+    "causal_off_by_one": ("_apply_masks", _causal_off_by_one),
+    "causal_bottom_right": ("_apply_masks", _causal_bottom_right),
+    "padding_ignored": ("_apply_masks", _padding_ignored),
+    "softmax_without_max_shift": ("_softmax_rows", _no_max_shift),
+    "softmax_sum_drops_last_key": ("_softmax_rows", _sum_drops_last_key),
+    "lse_ignores_max": ("_softmax_rows", _max_not_subtracted_back),
+    "values_transposed_weights": ("_weighted_values", lambda P, v: (P.T @ v[: P.shape[0]]) if P.shape[0] <= v.shape[0] else P @ v[::-1]),
+    "values_reversed": ("_weighted_values", lambda P, v: P @ v[::-1]),
+    "values_negated": ("_weighted_values", lambda P, v: -(P @ v)),
+    "lse_base2": ("_log_sum_exp", lambda M, L: np.where(np.isneginf(M), NEG_INF, M + np.log2(np.where(L > 0, L, 1)))),
+    "lse_without_max": ("_log_sum_exp", lambda M, L: np.where(np.isneginf(M), NEG_INF, np.log(np.where(L > 0, L, 1)))),
+    "lse_sign": ("_log_sum_exp", lambda M, L: np.where(np.isneginf(M), NEG_INF, M - np.log(np.where(L > 0, L, 1)))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    failed = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception as e:  # AssertionError or a shape error both mean "caught"
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"

@@ -1,0 +1,155 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module only draws numbers and rounds them to bfloat16. It holds none of
+the attention arithmetic, so both the CPU oracle and the GPU path can be fed
+from it without sharing any of the method's code.
+
+The five named workloads follow the shapes the pages use: the onecalc.app
+"Attention memory" worked example (one sequence, 32 heads, 4,096 and 8,192
+tokens, 16-bit scores), and the news.hamidun.com "Flash attention" glossary
+example of 32,000-token training sequences for a 7B model (s = 32768, H = 32,
+d = 128 stands in for that layer). Every tensor is drawn from N(0, 1) in
+float32 with NumPy's PCG64, then rounded to bfloat16 with round-to-nearest-even,
+so the oracle and the kernel see bit-identical values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "HEADLINE",
+    "round_to_bf16",
+    "bf16_bits_to_f32",
+    "generate",
+    "random_case",
+    "padding_mask_from_lengths",
+    "scale_for",
+]
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16, round-to-nearest-even.
+
+    Returns the 16-bit patterns (uint16). NaN stays a quiet NaN; +-inf stay.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    rounded = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        rounded = np.where(nan, ((u >> 16) | 0x40).astype(np.uint16), rounded)
+    return rounded
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to the exactly equal float32 values."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def scale_for(d: int) -> np.float32:
+    """The float32 value of 1/sqrt(d) that is handed to both sides."""
+    return np.float32(1.0 / math.sqrt(d))
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    s_q: int
+    s_k: int
+    d: int
+    causal: bool
+    padded: bool        # key padding mask with per-sequence valid length ~ U{s/2..s}
+    k_mult: float       # K drawn, multiplied in float32, then rounded once
+    seed: int
+
+    @property
+    def scale(self) -> np.float32:
+        return scale_for(self.d)
+
+    def flops(self) -> float:
+        """Metric FLOPs: 4*B*H*s_q*s_k*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.s_q * self.s_k * self.d
+        return f / 2.0 if self.causal else f
+
+
+WORKLOADS = (
+    Workload("B=1,H=1,s=128,d=64,dense", 1, 1, 128, 128, 64, False, False, 1.0, 44001),
+    Workload("B=1,H=32,s=4096,d=128,causal", 1, 32, 4096, 4096, 128, True, False, 1.0, 44002),
+    Workload("B=1,H=32,s=8192,d=128,causal", 1, 32, 8192, 8192, 128, True, False, 1.0, 44003),
+    Workload("B=4,H=16,s=2048,d=64,key-padding", 4, 16, 2048, 2048, 64, False, True, 1.0, 44004),
+    Workload("B=1,H=32,s=32768,d=128,causal,Kx3", 1, 32, 32768, 32768, 128, True, False, 3.0, 44005),
+)
+
+# The configuration the headline throughput is quoted on (s = 8192, d = 128, causal).
+HEADLINE = WORKLOADS[2]
+
+
+def padding_mask_from_lengths(lengths: np.ndarray, s_k: int) -> np.ndarray:
+    """uint8 [B, s_k]; 1 marks a padded key (j >= length of that sequence)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    return (np.arange(s_k)[None, :] >= lengths[:, None]).astype(np.uint8)
+
+
+def _draw(rng: np.random.Generator, shape, mult: float = 1.0) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if mult != 1.0:
+        x *= np.float32(mult)
+    return round_to_bf16(x)
+
+
+def generate(w: Workload, heads: Optional[slice] = None) -> dict:
+    """Draw Q, K, V (in that order), then the valid lengths, for one workload.
+
+    Returned arrays hold bfloat16 bit patterns (uint16, [B,H,s,d], contiguous).
+    ``heads`` optionally keeps a slice of the head axis after drawing (the draw
+    itself is always the full tensor so the values do not depend on it).
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    q = _draw(rng, (w.B, w.H, w.s_q, w.d))
+    k = _draw(rng, (w.B, w.H, w.s_k, w.d), w.k_mult)
+    v = _draw(rng, (w.B, w.H, w.s_k, w.d))
+    kpm = None
+    lengths = None
+    if w.padded:
+        lengths = rng.integers(w.s_k // 2, w.s_k, size=w.B, endpoint=True)
+        kpm = padding_mask_from_lengths(lengths, w.s_k)
+    if heads is not None:
+        q, k, v = (np.ascontiguousarray(t[:, heads]) for t in (q, k, v))
+    return dict(q=q, k=k, v=v, kpm=kpm, lengths=lengths, scale=w.scale,
+                causal=w.causal)
+
+
+def random_case(seed: int, B: int, H: int, s_q: int, s_k: int, d: int, *,
+                causal: bool = False, mask: str = "none", q_mult: float = 1.0,
+                k_mult: float = 1.0, scale: Optional[float] = None) -> dict:
+    """A seeded case of any shape, for edge and ragged tests.
+
+    mask: "none"; "lengths" (valid length per sequence ~ U{0..s_k}); "random"
+    (each key padded independently with probability 1/2, so the mask is not a
+    suffix); "all" (every key padded).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _draw(rng, (B, H, s_q, d), q_mult)
+    k = _draw(rng, (B, H, s_k, d), k_mult)
+    v = _draw(rng, (B, H, s_k, d))
+    kpm = None
+    if mask == "lengths":
+        lengths = rng.integers(0, s_k, size=B, endpoint=True)
+        kpm = padding_mask_from_lengths(lengths, s_k)
+    elif mask == "random":
+        kpm = (rng.random((B, s_k)) < 0.5).astype(np.uint8)
+    elif mask == "all":
+        kpm = np.ones((B, s_k), dtype=np.uint8)
+    elif mask != "none":
+        raise ValueError(f"unknown mask kind {mask!r}")
+    sc = scale_for(d) if scale is None else np.float32(scale)
+    return dict(q=q, k=k, v=v, kpm=kpm, scale=sc, causal=causal)
