@@ -1,0 +1,136 @@
+"""Python binding of the attention forward C ABI (include/attn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library libattn.so, built in-tree by exact_attention_44_amd.build. torch is
+used for device memory and the current stream, nothing else. There is no
+fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+from .build import LIB_PATH
+
+__all__ = [
+    "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
+    "ATTN_ERR_ALIAS", "ATTN_ERR_SCALE", "ATTN_ERR_LAUNCH", "AttnError", "load_library",
+    "attn_fwd", "attn_fwd_validate", "attn_status_str", "attn_last_hip_error", "fwd",
+    "LIB_PATH",
+]
+
+ATTN_OK = 0
+ATTN_ERR_NULL = 1
+ATTN_ERR_SHAPE = 2
+ATTN_ERR_HEAD_DIM = 3
+ATTN_ERR_ALIGN = 4
+ATTN_ERR_ALIAS = 5
+ATTN_ERR_SCALE = 6
+ATTN_ERR_LAUNCH = 7
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = attn_status_str(status)
+        if status == ATTN_ERR_LAUNCH:
+            msg += f" (hipError_t {attn_last_hip_error()})"
+        super().__init__(msg)
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is missing: build it with "
+            "`python -m exact_attention_44_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                             ctypes.c_float, ctypes.c_int, vp, vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_validate.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                      ctypes.c_float, ctypes.c_int, vp]
+    lib.attn_fwd_validate.restype = ctypes.c_int
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def attn_fwd(q, k, v, out, lse, B: int, H: int, s_q: int, s_k: int, d: int, scale: float,
+             causal: bool, key_padding_mask, stream) -> int:
+    """The C entry point with the same arguments. Tensors may be passed as
+    torch tensors or raw device addresses; stream as a hipStream_t handle (int)
+    or None. Returns the attn_status code."""
+    return load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                   B, H, s_q, s_k, d, float(scale), 1 if causal else 0,
+                                   _ptr(key_padding_mask), stream)
+
+
+def attn_fwd_validate(q, k, v, out, lse, B: int, H: int, s_q: int, s_k: int, d: int,
+                      scale: float, causal: bool, key_padding_mask) -> int:
+    return load_library().attn_fwd_validate(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                            B, H, s_q, s_k, d, float(scale),
+                                            1 if causal else 0, _ptr(key_padding_mask))
+
+
+def attn_status_str(status: int) -> str:
+    return load_library().attn_status_str(status).decode()
+
+
+def attn_last_hip_error() -> int:
+    return load_library().attn_last_hip_error()
+
+
+def fwd(q, k, v, *, causal: bool = False, key_padding_mask=None, scale: Optional[float] = None,
+        out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Attention forward on torch device tensors: q [B,H,s_q,d], k/v [B,H,s_k,d]
+    bf16 contiguous; key_padding_mask None or uint8/bool [B,s_k] (nonzero =
+    padded). Returns (out bf16 [B,H,s_q,d], lse float32 [B,H,s_q]). Runs on
+    torch's current stream of q's device."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise TypeError(f"{name} must be a 4-D bfloat16 torch tensor")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    B, H, s_q, d = q.shape
+    s_k = k.shape[2]
+    if tuple(k.shape) != (B, H, s_k, d) or tuple(v.shape) != (B, H, s_k, d):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if key_padding_mask is not None:
+        m = key_padding_mask
+        if m.dtype not in (torch.uint8, torch.bool) or tuple(m.shape) != (B, s_k):
+            raise ValueError("key_padding_mask must be uint8/bool [B, s_k]")
+        if not m.is_cuda or not m.is_contiguous():
+            raise ValueError("key_padding_mask must be a contiguous device tensor")
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(q.device):
+        if out is None:
+            out = torch.empty((B, H, s_q, d), dtype=torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, H, s_q), dtype=torch.float32, device=q.device)
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_fwd(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal, key_padding_mask, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, lse

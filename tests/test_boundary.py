@@ -1,0 +1,136 @@
+"""The C ABI on the host: the library loads, exports what include/attn.h
+declares, and rejects bad arguments before touching the HIP runtime."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_44_amd as E
+from exact_attention_44_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", src)))
+
+
+def header_enum():
+    src = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"\b(ATTN_[A-Z_]+)\s*=\s*(\d+)", src)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        pytest.fail(f"{LIB_PATH} not built (run python -m exact_attention_44_amd.build)")
+    return E.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert names == ["attn_fwd", "attn_fwd_validate", "attn_last_hip_error", "attn_status_str"]
+    for n in names:
+        assert hasattr(lib, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", dyn), f"{n} not exported"
+
+
+def test_library_never_allocates_device_memory():
+    und = subprocess.run(["nm", "-D", "--undefined-only", LIB_PATH], capture_output=True, text=True).stdout
+    assert "hipMalloc" not in und and "hipFree" not in und and "hipHostMalloc" not in und
+
+
+def test_status_codes_match_binding(lib):
+    enum = header_enum()
+    for k, v in enum.items():
+        assert getattr(E, k) == v, k
+    for v in enum.values():
+        assert E.attn_status_str(v).startswith("ATTN_")
+    assert E.attn_last_hip_error() == 0
+
+
+# Fake, well-aligned, non-overlapping device addresses: every call below is
+# rejected (or is empty) on the host, so nothing is dereferenced.
+Q, K, V, OUT, LSE, KPM = (1 << 40), (2 << 40), (3 << 40), (4 << 40), (5 << 40), (6 << 40)
+GOOD = dict(q=Q, k=K, v=V, out=OUT, lse=LSE, B=2, H=3, s_q=100, s_k=90, d=128, scale=0.1,
+            causal=1, key_padding_mask=KPM)
+
+
+def call(fn, **over):
+    a = dict(GOOD, **over)
+    args = [a[n] for n in ("q", "k", "v", "out", "lse", "B", "H", "s_q", "s_k", "d", "scale",
+                           "causal", "key_padding_mask")]
+    if fn is E.attn_fwd:
+        return fn(*args, None)
+    return fn(*args)
+
+
+@pytest.mark.parametrize("fn", [E.attn_fwd_validate, E.attn_fwd], ids=["validate", "fwd"])
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), E.ATTN_ERR_NULL),
+    (dict(out=None), E.ATTN_ERR_NULL),
+    (dict(lse=None), E.ATTN_ERR_NULL),
+    (dict(k=None), E.ATTN_ERR_NULL),
+    (dict(v=None), E.ATTN_ERR_NULL),
+    (dict(B=-1), E.ATTN_ERR_SHAPE),
+    (dict(s_k=-5), E.ATTN_ERR_SHAPE),
+    (dict(s_q=(1 << 22) + 1), E.ATTN_ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 12), E.ATTN_ERR_SHAPE),
+    (dict(d=96), E.ATTN_ERR_HEAD_DIM),
+    (dict(d=256), E.ATTN_ERR_HEAD_DIM),
+    (dict(q=Q + 8), E.ATTN_ERR_ALIGN),
+    (dict(out=OUT + 4), E.ATTN_ERR_ALIGN),
+    (dict(lse=LSE + 2), E.ATTN_ERR_ALIGN),
+    (dict(out=Q + 512), E.ATTN_ERR_ALIAS),
+    (dict(lse=V + 64), E.ATTN_ERR_ALIAS),
+    (dict(lse=OUT + 1024), E.ATTN_ERR_ALIAS),
+    (dict(out=KPM - 256), E.ATTN_ERR_ALIAS),
+    (dict(scale=float("nan")), E.ATTN_ERR_SCALE),
+    (dict(scale=float("inf")), E.ATTN_ERR_SCALE),
+])
+def test_rejected_before_launch(lib, fn, over, code):
+    assert call(fn, **over) == code
+
+
+def test_valid_arguments_pass_validation(lib):
+    assert call(E.attn_fwd_validate) == E.ATTN_OK
+    assert call(E.attn_fwd_validate, d=64, causal=0, key_padding_mask=None) == E.ATTN_OK
+    assert call(E.attn_fwd_validate, scale=0.0) == E.ATTN_OK
+    assert call(E.attn_fwd_validate, scale=-3.0) == E.ATTN_OK
+    # k, v may be NULL when there are no keys
+    assert call(E.attn_fwd_validate, k=None, v=None, s_k=0) == E.ATTN_OK
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(H=0), dict(s_q=0)])
+def test_empty_problems_are_no_ops(lib, over):
+    # nothing to compute: returns OK without launching, even with NULL buffers
+    null = dict(q=None, k=None, v=None, out=None, lse=None)
+    assert call(E.attn_fwd, **over, **null) == E.ATTN_OK
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        import importlib
+        mod = importlib.import_module("exact_attention_44_amd")
+        saved = mod._lib
+        mod._lib = None
+        try:
+            mod.load_library(str(tmp_path / "nope.so"))
+        finally:
+            mod._lib = saved
+
+
+def test_fwd_rejects_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        E.fwd(q, q, q)
+    with pytest.raises(TypeError):
+        E.fwd(q.float(), q, q)
