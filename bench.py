@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward on one MI355X.
+
+One step = one attn_fwd call (the whole path: score product, masks, online
+softmax, value product, log-sum-exp) over the s = 8192 workload
+(B=1, H=32, d=128, causal, seeded bf16 inputs already resident in device
+memory). Prints one JSON line:
+  value          metric FLOPs (4*B*H*s^2*d, halved for causal) per second of
+                 wall time over the timed steps, in TFLOP/s;
+  roofline       the kernel's average launch duration from HIP events recorded
+                 on the launch stream, against the bf16 dense MFMA peak;
+  cpu_baseline   the float64 CPU oracle, timed on a few heads of the same
+                 workload on this host.
+
+Options: --workload i selects another of the five workloads (for sweeps; the
+default line is the s = 8192 one); --calibrate-copy adds one plain device copy
+of known size after the timed region, so a counter profile of this command also
+holds the reference that scales FETCH_SIZE / WRITE_SIZE to bytes.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s at 1 MI355X (s=4096–32768) + % of bf16 MFMA peak"
+# MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+COPY_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="index into workloads.WORKLOADS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, g, target_s):
+    """Time the oracle on whole heads of the same workload until ~target_s."""
+    import numpy as np
+
+    from oracle import attention_fp64
+    from workloads import bf16_bits_to_f32
+
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            threads = blas[0]
+    except Exception:
+        pass
+    per_head = w.flops() / (w.B * w.H)
+    heads, spent = 0, 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            q, k, v = (bf16_bits_to_f32(g[n][b:b + 1, h:h + 1]) for n in ("q", "k", "v"))
+            kpm = None if g["kpm"] is None else g["kpm"][b:b + 1]
+            t0 = time.perf_counter()
+            attention_fp64(q, k, v, float(g["scale"]), w.causal, kpm)
+            spent += time.perf_counter() - t0
+            heads += 1
+            if spent >= target_s:
+                break
+        if spent >= target_s:
+            break
+    return {
+        "value": round(per_head * heads / spent / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"float64 NumPy oracle (materialises each head's s x s scores, row blocks "
+                   f"of 2048) on {heads} of {w.B * w.H} heads of {w.name}: {spent:.1f} s on "
+                   f"{threads} BLAS threads, {platform.processor() or platform.machine()}; "
+                   f"FLOPs counted with the metric formula"),
+    }
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
+              "the kernel shards over (batch, head) with no communication, so N GPUs run "
+              "the same single-GPU launch on their own heads.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_44_amd as E
+    from workloads import WORKLOADS
+
+    E.load_library()
+    w = WORKLOADS[a.workload]
+    from workloads import generate
+    g = generate(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (torch.from_numpy(g[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
+    kpm = None if g["kpm"] is None else torch.from_numpy(g["kpm"]).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.s_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    args = (q, k, v, out, lse, w.B, w.H, w.s_q, w.s_k, w.d, float(g["scale"]), w.causal, kpm,
+            stream.cuda_stream)
+
+    def step():
+        st = E.attn_fwd(*args)
+        if st != E.ATTN_OK:
+            raise E.AttnError(st)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+
+    if a.calibrate_copy:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    flops = w.flops()
+    value = flops * a.steps / wall / 1e12
+    achieved = flops / (kern_avg_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(wall / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "s_q": w.s_q, "s_k": w.s_k, "d": w.d,
+                   "causal": w.causal, "key_padding": w.padded, "seed": w.seed,
+                   "flops_per_step": flops},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "attn_fwd_kernel",
+            "kernel_avg_ms": round(kern_avg_ms, 5),
+            "kernel_min_ms": round(min(kern_ms), 5),
+        },
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, g, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -37,14 +37,19 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16, round-to-nearest-even.
 
     Returns the 16-bit patterns (uint16). NaN stays a quiet NaN; +-inf stay.
+    (u + 0x7FFF + lsb) cannot wrap 32 bits for any non-NaN pattern: the largest,
+    -inf = 0xFF800000, gives 0xFF807FFF.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    rounded = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    t = (u >> np.uint32(16)) & np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= np.uint32(16)
+    rounded = t.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        rounded = np.where(nan, ((u >> 16) | 0x40).astype(np.uint16), rounded)
+        rounded[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
     return rounded
 
 
