@@ -34,6 +34,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn.h"
 
 namespace {
@@ -63,16 +65,6 @@ struct FwdParams {
   uint32_t q_and;   // 0 when scale == 0: Q zeroed, scores are exactly 0
 };
 
-// XOR swizzle of 16-byte units for a row of U units. Rows of 256 B (U = 16)
-// permute by row & 15; narrower rows by the row's index within 256 B groups,
-// so any 16 consecutive rows read at one logical unit touch 16 distinct
-// 4-bank groups.
-template <int U>
-__device__ __forceinline__ int swz(int row) {
-  static_assert(U == 4 || U == 8 || U == 16, "unsupported LDS row width");
-  return (row / (16 / U)) & (U - 1);
-}
-
 // Key row fed to accumulator row m of the score MFMA (see file comment).
 __device__ __forceinline__ int key_of_row(int m) {
   const int a = m >> 3, hh = (m >> 2) & 1, b = m & 3;
@@ -83,6 +75,13 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// x *= a, written so the product stays in x's register. The rare O rescale
+// sits in a branch; a plain multiply lets the register allocator give the
+// merged value a second set of registers and copy all of O on every block.
+__device__ __forceinline__ void scale_in_place(float& x, float a) {
+  asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(a));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2_t f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
@@ -90,40 +89,55 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 // Buffer resource over [base, base + bytes): loads past the end return zero,
 // which pads ragged query and key tails without branches.
+// The fields are wave-uniform by construction; readfirstlane states that to
+// the compiler so the descriptor stays in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)n, 0x00020000);
 }
 
 __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
 
-template <int D, int NW, int KB, bool CAUSAL, bool PADMASK>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdParams p) {
-  constexpr int NT = NW * 64;
-  constexpr int BR = 32 * NW;         // query rows per workgroup, 32 per wave
-  constexpr int BC = 32 * KB;         // keys per tile
+template <int D, bool CAUSAL, bool PADMASK>
+__global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
+  constexpr int NT = 512;             // 8 waves: two ping-pong groups of 4
+  constexpr int BR = 256;             // query rows per workgroup, 32 per wave
+  constexpr int BC = 64;              // keys per tile
+  constexpr int KB = BC / 32;         // 32-key blocks per tile
   constexpr int DK = D / 16;          // k-steps of the score product
   constexpr int DB = D / 32;          // 32-column blocks of the output
   constexpr int KU = D / 8;           // 16-byte units per K row
-  constexpr int VU = BC / 8;          // 16-byte units per V^T row
-  constexpr int K_BYTES = BC * D * 2;
-  constexpr int BUF_BYTES = 2 * K_BYTES;
-  constexpr int K_LD = BC * KU / NT;  // 16-byte K loads per thread per tile
-  static_assert((BC * KU) % NT == 0, "K tile must split evenly over the threads");
-  // V is staged in items of VK keys x 8 columns (VK 16-byte loads, 8 LDS writes)
-  constexpr int VK = ((BC / 2) * (D / 8) > NT) ? 4 : 2;
-  constexpr int V_ITEMS = (BC / VK) * (D / 8);
-  constexpr int V_LD = (V_ITEMS + NT - 1) / NT;
-  constexpr int MB = (BC + 63) / 64;  // 64-key mask ballots per tile
+  // LDS rows are padded by 16 bytes: with these strides the 16 lanes of every
+  // fragment read hit 16 distinct 4-bank groups, and each lane's fragment
+  // addresses are one base plus compile-time offsets.
+  constexpr int KS = D * 2 + 16;      // K row stride (bytes)
+  constexpr int VS = BC * 2 + 16;     // V^T row stride (bytes)
+  constexpr int K_BYTES = BC * KS;
+  constexpr int BUF_BYTES = K_BYTES + D * VS;
+  constexpr int NBUF = 3;             // a tile is read during four phases
+  // Each group stages its half (32 keys) of a tile: K in 16-byte pieces, V in
+  // items of 2 keys x 8 columns (transposed on the way into LDS).
+  constexpr int GT = NT / 2;
+  constexpr int K_LD = 32 * KU / GT;
+  static_assert((32 * KU) % GT == 0, "K half tile must split evenly over a group");
+  constexpr int V_ITEMS = 16 * (D / 8);
+  constexpr int V_LD = (V_ITEMS + GT - 1) / GT;
+  constexpr float kSumLimit = 1048576.f;  // 2^20: see the softmax phase
 
-  __shared__ __attribute__((aligned(16))) char lds[2 * BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF_BYTES];
   __shared__ int lds_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv >> 2;            // waves w and w+4 share a SIMD
+  const int gt = tid & (GT - 1);
   const int hl = lane >> 5;
   const int ln = lane & 31;
 
@@ -135,8 +149,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdParams p) {
   const int s_q = p.s_q, s_k = p.s_k;
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (int64_t)bh * s_q * D, (uint32_t)s_q * D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (int64_t)bh * s_k * D, (uint32_t)s_k * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (int64_t)bh * s_k * D, (uint32_t)s_k * D * 2);
+  const uint16_t* kg = p.k + (int64_t)bh * s_k * D;
+  const uint16_t* vg = p.v + (int64_t)bh * s_k * D;
   const uint8_t* mg = PADMASK ? p.kpm + (int64_t)b * s_k : nullptr;
 
   // ---- keys this tile can see: causal stops at the last query row; padding
@@ -171,9 +185,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdParams p) {
   const int n_kv = (kend + BC - 1) / BC;
 
   // ---- Q fragments (B operand of the score product), kept in registers.
+  const int qlo = q0 + 32 * wv;  // first query row of this wave
   bf16x8_t qf[DK];
   {
-    const uint32_t row = (uint32_t)(q0 + 32 * wv + ln);
+    const uint32_t row = (uint32_t)(qlo + ln);
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
       u32x4_t x = load16(rq, (row * D + 16 * kk + 8 * hl) * 2);
@@ -182,230 +197,253 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // ---- tile staging: global -> registers -> LDS
+  // ---- staging of this group's half (keys 32*grp .. 32*grp+31) of a tile
   u32x4_t kr[K_LD];
-  u32x4_t vr[V_LD][VK];
-  uint32_t mbyte[MB];
-  uint64_t cur_mask[MB], next_mask[MB];
-#pragma unroll
-  for (int t = 0; t < MB; ++t) cur_mask[t] = next_mask[t] = 0;
-
-  auto load_tile = [&](int jt) {
-    const int j0 = jt * BC;
+  u32x4_t vr[V_LD][2];
+  auto load_half = [&](int u) {
+    const int j0 = u * BC;
+    // zero records past the end: a tile index beyond the last reads zeros
+    const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D * 2;
+    const __amdgpu_buffer_rsrc_t rkt = make_rsrc(kg + (int64_t)j0 * D, rest);
+    const __amdgpu_buffer_rsrc_t rvt = make_rsrc(vg + (int64_t)j0 * D, rest);
 #pragma unroll
     for (int i = 0; i < K_LD; ++i) {
-      const int id = i * NT + tid;
-      const int row = id / KU, u = id % KU;
-      kr[i] = load16(rk, ((uint32_t)(j0 + row) * D + 8 * u) * 2);
+      const int id = i * GT + gt;
+      const int row = 32 * grp + id / KU, un = id % KU;
+      kr[i] = load16(rkt, (uint32_t)(row * D + 8 * un) * 2);
     }
 #pragma unroll
     for (int i = 0; i < V_LD; ++i) {
-      const int id = i * NT + tid;
-      if ((V_ITEMS % NT) == 0 || id < V_ITEMS) {
-        const int kq = id % (BC / VK), dc = id / (BC / VK);
+      const int id = i * GT + gt;
+      if ((V_ITEMS % GT) == 0 || id < V_ITEMS) {
+        const int kq = id & 15, dc = id >> 4;
+        const int key = 32 * grp + 2 * kq;
 #pragma unroll
-        for (int r = 0; r < VK; ++r)
-          vr[i][r] = load16(rv, ((uint32_t)(j0 + VK * kq + r) * D + 8 * dc) * 2);
-      }
-    }
-    if (PADMASK) {
-#pragma unroll
-      for (int t = 0; t < MB; ++t) {
-        const int kl = 64 * t + lane, key = j0 + kl;
-        mbyte[t] = (kl < BC && key < s_k) ? (uint32_t)mg[key] : 1u;
+        for (int r = 0; r < 2; ++r) vr[i][r] = load16(rvt, (uint32_t)((key + r) * D + 8 * dc) * 2);
       }
     }
   };
-
-  auto store_tile = [&](int buf) {
-    char* kl = lds + buf * BUF_BYTES;
+  auto store_half = [&](int u) {
+    char* kl = lds + (u % NBUF) * BUF_BYTES;
     char* vl = kl + K_BYTES;
 #pragma unroll
     for (int i = 0; i < K_LD; ++i) {
-      const int id = i * NT + tid;
-      const int row = id / KU, u = id % KU;
-      *(u32x4_t*)(kl + row * (KU * 16) + ((u ^ swz<KU>(row)) << 4)) = kr[i];
+      const int id = i * GT + gt;
+      const int row = 32 * grp + id / KU, un = id % KU;
+      *(u32x4_t*)(kl + row * KS + un * 16) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < V_LD; ++i) {
-      const int id = i * NT + tid;
-      if ((V_ITEMS % NT) == 0 || id < V_ITEMS) {
-        const int kq = id % (BC / VK), dc = id / (BC / VK);
-        // Threads of one column chunk fill one V^T row; the next chunk's rows
-        // are 8 further down. Odd chunks walk their 8 rows in swapped pairs so
-        // neighbouring chunks write rows of opposite parity (other bank half).
-        const int odd = dc & 1;
-        const uint32_t sel_even = odd ? 0x07060302u : 0x05040100u;
-        const uint32_t sel_odd = odd ? 0x05040100u : 0x07060302u;
-        const int key_byte = VK * kq * 2;  // byte offset of this item's keys in a row
+      const int id = i * GT + gt;
+      if ((V_ITEMS % GT) == 0 || id < V_ITEMS) {
+        const int kq = id & 15, dc = id >> 4;
+        char* dst = vl + (8 * dc) * VS + (32 * grp + 2 * kq) * 2;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const int w = c >> 1;
-          const uint32_t sel = (c & 1) ? sel_odd : sel_even;
-          const int row = 8 * dc + (c ^ odd);
-          char* dst = vl + row * (VU * 16) + (((key_byte >> 4) ^ swz<VU>(row)) << 4) + (key_byte & 15);
-          if (VK == 4) {
-            u32x2_t val;
-            val[0] = __builtin_amdgcn_perm(vr[i][1][w], vr[i][0][w], sel);
-            val[1] = __builtin_amdgcn_perm(vr[i][3 % VK][w], vr[i][2 % VK][w], sel);
-            *(u32x2_t*)dst = val;
-          } else {
-            *(uint32_t*)dst = __builtin_amdgcn_perm(vr[i][1][w], vr[i][0][w], sel);
-          }
+          // column 8*dc + c of two consecutive key rows -> two consecutive keys
+          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+          *(uint32_t*)(dst + c * VS) = __builtin_amdgcn_perm(vr[i][1][c >> 1], vr[i][0][c >> 1], sel);
         }
       }
     }
-    if (PADMASK) {
-#pragma unroll
-      for (int t = 0; t < MB; ++t) next_mask[t] = __ballot(mbyte[t] != 0u);
-    }
   };
 
-  // ---- running statistics and output accumulator (O^T, one query per lane)
+  // ---- per-wave running state: O^T (one query per lane), row max, row sum
   f32x16_t o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t sc[KB];         // scores of the tile between its two phases
+  float ex[KB][16];        // exp2 of the scores, within a V step
+  bf16x8_t pf[KB][2];      // weights of the tile between its two phases
+  uint32_t mbyte = 1u;     // this lane's padding byte of the tile in flight
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16_t{};
 
-  const int k_lane_row = key_of_row(ln);
+  const int k_lane_off = key_of_row(ln) * KS + hl * 16;
+  const int v_lane_off = ln * VS + hl * 16;
   const float c = p.c;
-  const float lazy_thr = kLazy / c;  // kLazy in log2 units, as a raw-score margin
-  const int qlo = q0 + 32 * wv;      // first query row of this wave
 
-  if (n_kv > 0) {
-    load_tile(0);
-    store_tile(0);
+  // M step, first half: O^T += V_t^T P(t)^T (tile t in LDS buffer t % 3).
+  auto pv = [&](int t) {
+    const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + v_lane_off;
 #pragma unroll
-    for (int t = 0; t < MB; ++t) cur_mask[t] = next_mask[t];
-  }
-  __syncthreads();
-
-  for (int jt = 0; jt < n_kv; ++jt) {
-    const int buf = jt & 1;
-    const bool has_next = jt + 1 < n_kv;
-    if (has_next) load_tile(jt + 1);
-
-    const char* kl = lds + buf * BUF_BYTES;
-    const char* vl = kl + K_BYTES;
-    const int j0 = jt * BC;
-
-    // Hidden-key bits per 32-key block (padding and keys past s_k). These and
-    // the causal test below are wave-uniform: interior tiles take no masking
-    // branch at all.
-    uint32_t mw[KB];
-    bool any_mw = false;
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if (PADMASK) {
-        mw[kb] = (uint32_t)(cur_mask[kb >> 1] >> (32 * (kb & 1)));
-      } else {
-        const int rem = s_k - (j0 + 32 * kb);
-        mw[kb] = rem >= 32 ? 0u : (rem <= 0 ? ~0u : ~((1u << rem) - 1u));
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8_t a[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          a[db] = *(const bf16x8_t*)(vl + db * 32 * VS + (4 * kb + 2 * ks) * 16);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = mfma(a[db], pf[kb][ks], o[db]);
       }
-      any_mw = any_mw || (mw[kb] != 0u);
-    }
-
-    // S^T = K Q^T
-    f32x16_t s[KB];
+  };
+  // M step, second half: S(t)^T = K_t Q^T.
+  auto qk = [&](int t) {
+    const char* kl = lds + (t % NBUF) * BUF_BYTES + k_lane_off;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int row = 32 * kb + k_lane_row;
       bf16x8_t a[DK];
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk)
-        a[kk] = *(const bf16x8_t*)(kl + row * (KU * 16) + (((2 * kk + hl) ^ swz<KU>(row)) << 4));
-      s[kb] = f32x16_t{};
+      for (int kk = 0; kk < DK; ++kk) a[kk] = *(const bf16x8_t*)(kl + kb * 32 * KS + kk * 32);
+      f32x16_t acc = {};
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) s[kb] = mfma(a[kk], qf[kk], s[kb]);
+      for (int kk = 0; kk < DK; ++kk) acc = mfma(a[kk], qf[kk], acc);
+      sc[kb] = acc;
     }
-
-    // masks
-    if (CAUSAL && j0 + BC - 1 > qlo) {
-      const int lim = qlo + ln - j0;  // key offset in tile visible iff <= lim
+    if (PADMASK) {
+      const int key = t * BC + lane;
+      mbyte = key < s_k ? (uint32_t)mg[key] : 1u;
+    }
+  };
+  // V step: masks and online softmax of S(t) -> P(t); then this group's
+  // staging (store its half of tile u, load its half of tile u + 1).
+  auto vstep = [&](int t) {
+    const int j0 = t * BC;
+    // hidden-key bits of the tile (padding, keys past s_k); wave-uniform
+    uint64_t hid;
+    if (PADMASK) {
+      hid = __ballot(mbyte != 0u);
+    } else {
+      const int rem = s_k - j0;
+      hid = rem >= BC ? 0ull : ~((1ull << rem) - 1ull);
+    }
+    if (hid != 0ull || (CAUSAL && j0 + BC - 1 > qlo)) {
+      const int lim = qlo + ln - j0;  // causal: key offset visible iff <= lim
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint32_t sh = (uint32_t)(hid >> (32 * kb)) >> (8 * hl);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ko = 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
+          const bool hide = ((sh >> (16 * (r >> 3) + (r & 7))) & 1u) || (CAUSAL && ko > lim);
+          if (hide) sc[kb][r] = -INFINITY;
+        }
+      }
+    }
+    // Reference max: taken from the data on a row's first visible tile (O
+    // and l are still zero there). Afterwards it moves only when the tile's
+    // exp2 sum shows a score more than ~20 (log2 units) above it, i.e. the
+    // sum exceeds 2^20 or overflows; then O and l are rescaled and the tile
+    // is recomputed. O / l is the same for any reference.
+    if (__ballot(m_run == -INFINITY) != 0ull) {
+      float mx = sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (m_run == -INFINITY) m_run = mx;
+    }
+    float nmc = -((m_run == -INFINITY) ? 0.f : m_run) * c;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, nmc));
+        rs += e;
+        ex[kb][r] = e;
+      }
+    if (__ballot(!(rs <= kSumLimit)) != 0ull) {
+      float mx = sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = o[db][r];
+          scale_in_place(x, alpha);
+          o[db][r] = x;
+        }
+      l_run *= alpha;
+      m_run = m_new;
+      nmc = -m_new * c;
+      rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ko = 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
-          if (ko > lim) s[kb][r] = -INFINITY;
+          const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, nmc));
+          rs += e;
+          ex[kb][r] = e;
         }
     }
-    if (any_mw) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const uint32_t sh = mw[kb] >> (8 * hl);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if ((sh >> (16 * (r >> 3) + (r & 7))) & 1u) s[kb][r] = -INFINITY;
-      }
-    }
-
-    // online softmax
-    float mx = -INFINITY;
+    l_run += rs;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Lazy reference: move m only when the block max passes it by more than
-    // kLazy (log2 units). Weights exp2((s - m) c) then stay <= 2^kLazy and the
-    // final O / l is unchanged, while the output rescale becomes a rare,
-    // wave-uniform branch (always skipped on the row's first visible block,
-    // where O and l are still zero).
-    const bool move = mx > m_run + lazy_thr;
-    const float m_new = move ? mx : m_run;
-    const float alpha = move ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;
-    const bool rescale = move && (m_run != -INFINITY);
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float nmc = -m_ref * c;
-    float rs = 0.f;
-    bf16x8_t pf[KB][2];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, nmc));
-        rs += e;
-        s[kb][r] = e;
-      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         u32x4_t w;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2)
-          w[e2] = pack_bf16(s[kb][8 * ks + 2 * e2], s[kb][8 * ks + 2 * e2 + 1]);
+          w[e2] = pack_bf16(ex[kb][8 * ks + 2 * e2], ex[kb][8 * ks + 2 * e2 + 1]);
         pf[kb][ks] = __builtin_bit_cast(bf16x8_t, w);
       }
-    }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-    if (__ballot(rescale) != 0ull) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    }
+    // Staging is unconditional: past the last tile the loads read zeros and
+    // the stores land in a buffer no phase reads any more.
+    const int u = t + 1 + grp;
+    store_half(u);
+    load_half(u + 1);
+  };
 
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8_t a[DB];
-        const int u = 4 * kb + 2 * ks + hl;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int row = 32 * db + ln;
-          a[db] = *(const bf16x8_t*)(vl + row * (VU * 16) + ((u ^ swz<VU>(row)) << 4));
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma(a[db], pf[kb][ks], o[db]);
-      }
-    }
+  if (n_kv > 0) {
+    load_half(0);
+    store_half(0);
+    load_half(1);
+  }
+  __syncthreads();
 
-    if (has_next) {
-      store_tile(buf ^ 1);
-#pragma unroll
-      for (int t = 0; t < MB; ++t) cur_mask[t] = next_mask[t];
+  // ---- ping-pong phases (2 * n_kv + 2, each closed by a barrier). Group 0
+  // runs  M(0) V(0) M(1) V(1) ... V(n-1) M(n),  group 1 the same one phase
+  // later, where M(t) = [PV(t-1), QK(t)] runs on the matrix cores and V(t) =
+  // softmax of S(t) plus staging runs on the vector ALU. Waves w and w + 4
+  // share a SIMD, so every SIMD holds one wave in an M step and one in a V
+  // step and the two units overlap. Tile u is written by group 1 in phase
+  // 2u - 2 and group 0 in phase 2u - 1, and read in phases 2u .. 2u + 3:
+  // three LDS buffers.
+  if (grp == 0) {
+    if (n_kv > 0) qk(0);
+    __syncthreads();
+    for (int t = 0; t < n_kv - 1; ++t) {
+      vstep(t);
+      __syncthreads();
+      pv(t);
+      qk(t + 1);
+      __syncthreads();
     }
+    if (n_kv > 0) {
+      vstep(n_kv - 1);
+      __syncthreads();
+      pv(n_kv - 1);
+      __syncthreads();
+    }
+    __syncthreads();
+  } else {
+    store_half(1);  // V(-1): staging only
+    load_half(2);
+    __syncthreads();
+    if (n_kv > 0) {
+      qk(0);
+      __syncthreads();
+      vstep(0);
+      __syncthreads();
+    }
+    for (int t = 1; t < n_kv; ++t) {
+      pv(t - 1);
+      qk(t);
+      __syncthreads();
+      vstep(t);
+      __syncthreads();
+    }
+    if (n_kv > 0) pv(n_kv - 1);
     __syncthreads();
   }
 
@@ -434,35 +472,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdParams p) {
   }
 }
 
-// Tile shape per head dimension: NW waves of 32 query rows, KB blocks of 32 keys.
-template <int D>
-struct Cfg;
-template <>
-struct Cfg<128> {
-  static constexpr int NW = 8, KB = 2;
-};
-template <>
-struct Cfg<64> {
-  static constexpr int NW = 8, KB = 2;
-};
-
+// Rows of queries per workgroup (8 waves x 32).
 template <int D>
 constexpr int rows_per_block() {
-  return 32 * Cfg<D>::NW;
-}
-
-template <int D>
-constexpr int threads_per_block() {
-  return 64 * Cfg<D>::NW;
+  return 256;
 }
 
 thread_local int g_last_hip_error = 0;
 
 template <int D, bool CAUSAL, bool PADMASK>
 hipError_t launch(const FwdParams& p, int grid, hipStream_t stream) {
-  using C = Cfg<D>;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, C::NW, C::KB, CAUSAL, PADMASK>), dim3(grid),
-                     dim3(C::NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, PADMASK>), dim3(grid), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
