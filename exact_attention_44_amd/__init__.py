@@ -50,6 +50,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"HIP library {path} is missing: build it with "
             "`python -m exact_attention_44_amd.build` (hipcc, gfx950)")
+    # torch bundles its own HIP runtime; load it first so the process holds a
+    # single runtime (the library's libamdhip64 dependency then resolves to it)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,

@@ -49,7 +49,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.0f;  // see the online-softmax step in the kernel
 
 struct FwdParams {
   const uint16_t* q;
@@ -73,13 +72,6 @@ __device__ __forceinline__ int key_of_row(int m) {
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// x *= a, written so the product stays in x's register. The rare O rescale
-// sits in a branch; a plain multiply lets the register allocator give the
-// merged value a second set of registers and copy all of O on every block.
-__device__ __forceinline__ void scale_in_place(float& x, float a) {
-  asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(a));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -297,6 +289,23 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       mbyte = key < s_k ? (uint32_t)mg[key] : 1u;
     }
   };
+  // One M step: value product of tile tp, then score product of tile tq,
+  // software-pipelined so LDS fragment reads run LA fragments ahead of the
+  // MFMAs that consume them (an LDS read takes several MFMA durations).
+  constexpr int N_MF = KB * 2 * DB + KB * DK;  // MFMAs (= fragment reads) per M step
+  constexpr int LA = 6;
+  auto m_step = [&](int tp, int tq) {
+    pv(tp);
+    qk(tq);
+    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < N_MF - LA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the M step inside its phase
+  };
   // V step: masks and online softmax of S(t) -> P(t); then this group's
   // staging (store its half of tile u, load its half of tile u + 1).
   auto vstep = [&](int t) {
@@ -337,15 +346,20 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       if (m_run == -INFINITY) m_run = mx;
     }
     float nmc = -((m_run == -INFINITY) ? 0.f : m_run) * c;
-    float rs = 0.f;
+    // exp2 of the scores and their sum (four partial sums: short chains)
+    auto exps = [&]() -> float {
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, nmc));
-        rs += e;
-        ex[kb][r] = e;
-      }
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, nmc));
+          ps[r & 3] += e;
+          ex[kb][r] = e;
+        }
+      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+    float rs = exps();
     if (__ballot(!(rs <= kSumLimit)) != 0ull) {
       float mx = sc[0][0];
 #pragma unroll
@@ -359,22 +373,12 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = o[db][r];
-          scale_in_place(x, alpha);
-          o[db][r] = x;
+          o[db][r] *= alpha;
         }
       l_run *= alpha;
       m_run = m_new;
       nmc = -m_new * c;
-      rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, nmc));
-          rs += e;
-          ex[kb][r] = e;
-        }
+      rs = exps();
     }
     l_run += rs;
 #pragma unroll
@@ -415,8 +419,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     for (int t = 0; t < n_kv - 1; ++t) {
       vstep(t);
       __syncthreads();
-      pv(t);
-      qk(t + 1);
+      m_step(t, t + 1);
       __syncthreads();
     }
     if (n_kv > 0) {
@@ -437,8 +440,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       __syncthreads();
     }
     for (int t = 1; t < n_kv; ++t) {
-      pv(t - 1);
-      qk(t);
+      m_step(t - 1, t);
       __syncthreads();
       vstep(t);
       __syncthreads();
