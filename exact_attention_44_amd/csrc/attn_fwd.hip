@@ -246,7 +246,6 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t sc[KB];         // scores of the tile between its two phases
-  float ex[KB][16];        // exp2 of the scores, within a V step
   bf16x8_t pf[KB][2];      // weights of the tile between its two phases
   uint32_t mbyte = 1u;     // this lane's padding byte of the tile in flight
 #pragma unroll
@@ -297,6 +296,12 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   auto m_step = [&](int tp, int tq) {
     pv(tp);
     qk(tq);
+    // this group's staging: its half of tile tq + 1 into LDS, then the
+    // global loads of its half of tile tq + 2. Unconditional: past the last
+    // tile the loads read zeros and the stores land in a buffer that no phase
+    // reads any more.
+    store_half(tq + 1);
+    load_half(tq + 2);
     __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS reads
 #pragma unroll
     for (int i = 0; i < N_MF - LA; ++i) {
@@ -306,8 +311,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
     __builtin_amdgcn_sched_barrier(0);  // keep the M step inside its phase
   };
-  // V step: masks and online softmax of S(t) -> P(t); then this group's
-  // staging (store its half of tile u, load its half of tile u + 1).
+  // V step: masks and online softmax of S(t) -> P(t).
   auto vstep = [&](int t) {
     const int j0 = t * BC;
     // hidden-key bits of the tile (padding, keys past s_k); wave-uniform
@@ -346,20 +350,39 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       if (m_run == -INFINITY) m_run = mx;
     }
     float nmc = -((m_run == -INFINITY) ? 0.f : m_run) * c;
-    // exp2 of the scores and their sum (four partial sums: short chains)
-    auto exps = [&]() -> float {
+    // Weights P = exp2(s c - m c): float32 for the row sum, rounded to bf16
+    // as the value product's operand. Written as three independent batches
+    // (all FMAs, all exp2, then sums and packs) so a lone wave always has an
+    // independent instruction to issue instead of waiting on the previous
+    // result; the row sum uses four chains.
+    auto weights = [&]() -> float {
+      float x[KB][16];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(sc[kb][r], c, nmc);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[kb][r] = __builtin_amdgcn_exp2f(x[kb][r]);
       float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, nmc));
-          ps[r & 3] += e;
-          ex[kb][r] = e;
+        for (int r = 0; r < 16; ++r) ps[r & 3] += x[kb][r];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4_t w;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2)
+            w[e2] = pack_bf16(x[kb][8 * ks + 2 * e2], x[kb][8 * ks + 2 * e2 + 1]);
+          pf[kb][ks] = __builtin_bit_cast(bf16x8_t, w);
         }
       return (ps[0] + ps[1]) + (ps[2] + ps[3]);
     };
-    float rs = exps();
+    float rs = weights();
     if (__ballot(!(rs <= kSumLimit)) != 0ull) {
       float mx = sc[0][0];
 #pragma unroll
@@ -378,24 +401,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       l_run *= alpha;
       m_run = m_new;
       nmc = -m_new * c;
-      rs = exps();
+      rs = weights();
     }
     l_run += rs;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4_t w;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          w[e2] = pack_bf16(ex[kb][8 * ks + 2 * e2], ex[kb][8 * ks + 2 * e2 + 1]);
-        pf[kb][ks] = __builtin_bit_cast(bf16x8_t, w);
-      }
-    // Staging is unconditional: past the last tile the loads read zeros and
-    // the stores land in a buffer no phase reads any more.
-    const int u = t + 1 + grp;
-    store_half(u);
-    load_half(u + 1);
   };
 
   if (n_kv > 0) {
@@ -407,46 +415,60 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
 
   // ---- ping-pong phases (2 * n_kv + 2, each closed by a barrier). Group 0
   // runs  M(0) V(0) M(1) V(1) ... V(n-1) M(n),  group 1 the same one phase
-  // later, where M(t) = [PV(t-1), QK(t)] runs on the matrix cores and V(t) =
-  // softmax of S(t) plus staging runs on the vector ALU. Waves w and w + 4
+  // later, where M(t) = [PV(t-1), QK(t), staging] issues the matrix-core work
+  // (plus LDS stores and global loads, which fit between its MFMAs) and
+  // V(t) = the softmax of S(t) runs on the vector ALU. Waves w and w + 4
   // share a SIMD, so every SIMD holds one wave in an M step and one in a V
-  // step and the two units overlap. Tile u is written by group 1 in phase
-  // 2u - 2 and group 0 in phase 2u - 1, and read in phases 2u .. 2u + 3:
+  // step and the two units overlap. Tile u is written by group 0 in phase
+  // 2u - 2 and group 1 in phase 2u - 1, and read in phases 2u .. 2u + 3:
   // three LDS buffers.
-  if (grp == 0) {
-    if (n_kv > 0) qk(0);
+  // Phase boundary. The barrier orders memory only; the scheduling fences on
+  // both sides also keep register-only work in its phase (otherwise the
+  // compiler sinks the softmax into the next M step to fill MFMA gaps, and
+  // each wave ends up doing both kinds of work serially).
+  auto phase_sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (grp == 0) {
+    if (n_kv > 0) {
+      qk(0);
+      store_half(1);
+      load_half(2);
+    }
+    phase_sync();
     for (int t = 0; t < n_kv - 1; ++t) {
       vstep(t);
-      __syncthreads();
+      phase_sync();
       m_step(t, t + 1);
-      __syncthreads();
+      phase_sync();
     }
     if (n_kv > 0) {
       vstep(n_kv - 1);
-      __syncthreads();
+      phase_sync();
       pv(n_kv - 1);
-      __syncthreads();
+      phase_sync();
     }
-    __syncthreads();
+    phase_sync();
   } else {
-    store_half(1);  // V(-1): staging only
-    load_half(2);
-    __syncthreads();
+    phase_sync();  // phase 0: group 0 alone
     if (n_kv > 0) {
       qk(0);
-      __syncthreads();
+      store_half(1);
+      load_half(2);
+      phase_sync();
       vstep(0);
-      __syncthreads();
+      phase_sync();
     }
     for (int t = 1; t < n_kv; ++t) {
       m_step(t - 1, t);
-      __syncthreads();
+      phase_sync();
       vstep(t);
-      __syncthreads();
+      phase_sync();
     }
     if (n_kv > 0) pv(n_kv - 1);
-    __syncthreads();
+    phase_sync();
   }
 
   // ---- epilogue: O = O^T / l, lse = m * |scale| + ln(l)
