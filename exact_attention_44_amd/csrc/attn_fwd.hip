@@ -294,6 +294,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int N_MF = KB * 2 * DB + KB * DK;  // MFMAs (= fragment reads) per M step
   constexpr int LA = 6;
   auto m_step = [&](int tp, int tq) {
+    __builtin_amdgcn_s_setprio(2);
     pv(tp);
     qk(tq);
     // this group's staging: its half of tile tq + 1 into LDS, then the
@@ -310,6 +311,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
     __builtin_amdgcn_sched_barrier(0);  // keep the M step inside its phase
+    __builtin_amdgcn_s_setprio(0);
   };
   // V step: masks and online softmax of S(t) -> P(t).
   auto vstep = [&](int t) {
