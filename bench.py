@@ -12,7 +12,9 @@ memory). Prints one JSON line:
   cpu_baseline   the float64 CPU oracle, timed on a few heads of the same
                  workload on this host.
 
-Options: --workload i selects another of the five workloads (for sweeps; the
+Before the W warm-up steps, --ramp-ms (default 100) of untimed back-to-back
+steps bring the GPU to its sustained clock; the timed region is exactly K
+steps. Options: --workload i selects another of the five workloads (for sweeps; the
 default line is the s = 8192 one); --calibrate-copy adds one plain device copy
 of known size after the timed region, so a counter profile of this command also
 holds the reference that scales FETCH_SIZE / WRITE_SIZE to bytes.
@@ -37,8 +39,11 @@ COPY_BYTES = 1 << 30
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--ramp-ms", type=float, default=100.0,
+                    help="untimed back-to-back steps before the warm-up steps, so the "
+                         "GPU reaches its sustained clock (it needs ~25 ms of load)")
     ap.add_argument("--workload", type=int, default=2, help="index into workloads.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -122,6 +127,13 @@ def main():
         if st != E.ATTN_OK:
             raise E.AttnError(st)
 
+    t_ramp = time.perf_counter()
+    ramp_steps = 0
+    while (time.perf_counter() - t_ramp) * 1e3 < a.ramp_ms:
+        for _ in range(5):
+            step()
+        ramp_steps += 5
+        torch.cuda.synchronize()
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -155,6 +167,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "ramp_steps": ramp_steps,
         "ms_per_step": round(wall / a.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
