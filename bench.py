@@ -9,6 +9,9 @@ memory). Prints one JSON line:
                  wall time over the timed steps, in TFLOP/s;
   roofline       the kernel's average launch duration from HIP events recorded
                  on the launch stream, against the bf16 dense MFMA peak;
+                 its traffic is the HBM bytes per launch from rocprofv3
+                 FETCH_SIZE / WRITE_SIZE passes, null once the kernel source
+                 differs from the one they were taken on;
   cpu_baseline   the float64 CPU oracle, timed on a few heads of the same
                  workload on this host.
 
@@ -34,6 +37,19 @@ METRIC = "attention fwd TFLOP/s at 1 MI355X (s=4096–32768) + % of bf16 MFMA pe
 # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 COPY_BYTES = 1 << 30
+KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_fwd.hip")
+
+# HBM bytes per launch from two rocprofv3 counter passes (FETCH_SIZE, then
+# WRITE_SIZE) of this script, each scaled by what the same counter reports for
+# a 1 GiB copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0). Valid only for the kernel
+# source they were taken on: reported as null once the source's hash differs.
+MEASURED_TRAFFIC = {
+    "B=1,H=32,s=8192,d=128,causal": {
+        "source_sha256": "68234f4d8001f10f2974beefc45434caf35ac29ec0f1d88a1419a66034aa5f88",
+        "fetch_bytes": 466055622,
+        "write_bytes": 71314904,
+    },
+}
 
 
 def parse():
@@ -158,6 +174,19 @@ def main():
         torch.cuda.synchronize()
 
     flops = w.flops()
+    algorithmic_bytes = 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d + 2 * w.B * w.H * w.s_q * w.d \
+        + 4 * w.B * w.H * w.s_q
+    traffic, traffic_detail = None, {"algorithmic_bytes": algorithmic_bytes}
+    measured = MEASURED_TRAFFIC.get(w.name)
+    if measured is not None:
+        import hashlib
+        with open(KERNEL_SOURCE, "rb") as f:
+            current = hashlib.sha256(f.read()).hexdigest()
+        if current == measured["source_sha256"]:
+            traffic = measured["fetch_bytes"] + measured["write_bytes"]
+            traffic_detail.update(fetch_bytes=measured["fetch_bytes"],
+                                  write_bytes=measured["write_bytes"],
+                                  source_sha256=current)
     value = flops * a.steps / wall / 1e12
     achieved = flops / (kern_avg_ms * 1e-3) / 1e12
     res = {
@@ -184,7 +213,9 @@ def main():
             "peak": round(PEAK_BF16_TFLOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "bytes per launch",
+            "traffic_detail": traffic_detail,
             "kernel": "attn_fwd_kernel",
             "kernel_avg_ms": round(kern_avg_ms, 5),
             "kernel_min_ms": round(min(kern_ms), 5),

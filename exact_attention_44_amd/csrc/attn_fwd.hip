@@ -26,10 +26,11 @@
 // lane too, so the rescale by exp(m_old - m_new) is a per-lane scalar.
 //
 // LDS: K tile row-major [BC][D], V tile transposed [D][BC] (the transpose is
-// done in registers while storing), both with an XOR swizzle of 16-byte units
-// so the 16 lanes that share an LDS cycle hit distinct banks. Two buffers: the
-// next tile's global loads are issued before the current tile's math, stored
-// after it, one barrier per tile.
+// done in registers while storing), rows padded by 16 bytes so every 16-lane
+// fragment read hits distinct banks. Three buffers; the two wave groups take
+// turns (ping-pong): while one group's waves run matrix products and stage
+// tiles, the other group's waves run the softmax, and each SIMD holds one wave
+// of each group. Phases are separated by workgroup barriers.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
