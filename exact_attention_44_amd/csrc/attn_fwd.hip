@@ -27,10 +27,12 @@
 //
 // LDS: K tile row-major [BC][D], V tile transposed [D][BC] (the transpose is
 // done in registers while storing), rows padded by 16 bytes so every 16-lane
-// fragment read hits distinct banks. Three buffers; the two wave groups take
-// turns (ping-pong): while one group's waves run matrix products and stage
-// tiles, the other group's waves run the softmax, and each SIMD holds one wave
-// of each group. Phases are separated by workgroup barriers.
+// fragment read hits distinct banks. Four buffers. The two wave groups take
+// turns (ping-pong): while one group's waves run the matrix products, the
+// other group's waves run the softmax, and each SIMD holds one wave of each
+// group, because a wave's own vector instructions do not overlap its own
+// MFMAs while those of another wave on the SIMD do. Phases are separated by
+// workgroup barriers.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int VS = BC * 2 + 16;     // V^T row stride (bytes)
   constexpr int K_BYTES = BC * KS;
   constexpr int BUF_BYTES = K_BYTES + D * VS;
-  constexpr int NBUF = 3;             // a tile is read during four phases
+  constexpr int NBUF = 4;             // see the phase schedule below
   // Each group stages its half (32 keys) of a tile: K in 16-byte pieces, V in
   // items of 2 keys x 8 columns (transposed on the way into LDS).
   constexpr int GT = NT / 2;
@@ -193,18 +195,21 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // ---- staging of this group's half (keys 32*grp .. 32*grp+31) of a tile
   u32x4_t kr[K_LD];
   u32x4_t vr[V_LD][2];
-  auto load_half = [&](int u) {
+  auto load_k = [&](int u) {
     const int j0 = u * BC;
-    // zero records past the end: a tile index beyond the last reads zeros
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D * 2;
     const __amdgpu_buffer_rsrc_t rkt = make_rsrc(kg + (int64_t)j0 * D, rest);
-    const __amdgpu_buffer_rsrc_t rvt = make_rsrc(vg + (int64_t)j0 * D, rest);
 #pragma unroll
     for (int i = 0; i < K_LD; ++i) {
       const int id = i * GT + gt;
       const int row = 32 * grp + id / KU, un = id % KU;
       kr[i] = load16(rkt, (uint32_t)(row * D + 8 * un) * 2);
     }
+  };
+  auto load_v = [&](int u) {
+    const int j0 = u * BC;
+    const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D * 2;
+    const __amdgpu_buffer_rsrc_t rvt = make_rsrc(vg + (int64_t)j0 * D, rest);
 #pragma unroll
     for (int i = 0; i < V_LD; ++i) {
       const int id = i * GT + gt;
@@ -216,15 +221,17 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       }
     }
   };
-  auto store_half = [&](int u) {
+  auto store_k = [&](int u) {
     char* kl = lds + (u % NBUF) * BUF_BYTES;
-    char* vl = kl + K_BYTES;
 #pragma unroll
     for (int i = 0; i < K_LD; ++i) {
       const int id = i * GT + gt;
       const int row = 32 * grp + id / KU, un = id % KU;
       *(u32x4_t*)(kl + row * KS + un * 16) = kr[i];
     }
+  };
+  auto store_v = [&](int u) {
+    char* vl = lds + (u % NBUF) * BUF_BYTES + K_BYTES;
 #pragma unroll
     for (int i = 0; i < V_LD; ++i) {
       const int id = i * GT + gt;
@@ -233,13 +240,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
         char* dst = vl + (8 * dc) * VS + (32 * grp + 2 * kq) * 2;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          // column 8*dc + c of two consecutive key rows -> two consecutive keys
           const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
           *(uint32_t*)(dst + c * VS) = __builtin_amdgcn_perm(vr[i][1][c >> 1], vr[i][0][c >> 1], sel);
         }
       }
     }
   };
+  auto load_half = [&](int u) { load_k(u); load_v(u); };
+  auto store_half = [&](int u) { store_k(u); store_v(u); };
 
   // ---- per-wave running state: O^T (one query per lane), row max, row sum
   f32x16_t o[DB];
@@ -256,17 +264,29 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   const int v_lane_off = ln * VS + hl * 16;
   const float c = p.c;
 
-  // M step, first half: O^T += V_t^T P(t)^T (tile t in LDS buffer t % 3).
-  auto pv = [&](int t) {
+  // The first LA fragments of each value product are read at the end of the
+  // V step before it (see vstep_sync), so the M step starts on data that is
+  // already in registers instead of waiting for the LDS latency.
+  constexpr int LA = 6;               // fragment reads in flight in an M step
+  bf16x8_t vpre[LA];
+  auto v_frag = [&](int t, int i) -> bf16x8_t {
+    // fragment i of tile t's value product: kb = i / 8, ks = (i / 4) & 1, db = i & 3
     const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + v_lane_off;
+    const int kb = i / (2 * DB), ks = (i / DB) & 1, db = i % DB;
+    return *(const bf16x8_t*)(vl + db * 32 * VS + (4 * kb + 2 * ks) * 16);
+  };
+  // M step, first half: O^T += V_t^T P(t)^T (tile t in LDS buffer t % NBUF).
+  auto pv = [&](int t) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8_t a[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          a[db] = *(const bf16x8_t*)(vl + db * 32 * VS + (4 * kb + 2 * ks) * 16);
+        for (int db = 0; db < DB; ++db) {
+          const int i = (kb * 2 + ks) * DB + db;
+          a[db] = i < LA ? vpre[i < LA ? i : 0] : v_frag(t, i);
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] = mfma(a[db], pf[kb][ks], o[db]);
       }
@@ -293,18 +313,13 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // software-pipelined so LDS fragment reads run LA fragments ahead of the
   // MFMAs that consume them (an LDS read takes several MFMA durations).
   constexpr int N_MF = KB * 2 * DB + KB * DK;  // MFMAs (= fragment reads) per M step
-  constexpr int LA = 6;
+  static_assert(LA <= 2 * DB * KB, "prefetched fragments must belong to the value product");
   auto m_step = [&](int tp, int tq) {
     __builtin_amdgcn_s_setprio(2);
     pv(tp);
     qk(tq);
-    // this group's staging: its half of tile tq + 1 into LDS, then the
-    // global loads of its half of tile tq + 2. Unconditional: past the last
-    // tile the loads read zeros and the stores land in a buffer that no phase
-    // reads any more.
-    store_half(tq + 1);
-    load_half(tq + 2);
-    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS reads
+    store_v(tq + 1);
+    load_v(tq + 2);
 #pragma unroll
     for (int i = 0; i < N_MF - LA; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -316,6 +331,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   };
   // V step: masks and online softmax of S(t) -> P(t).
   auto vstep = [&](int t) {
+    store_k(t + 2);
+    load_k(t + 3);
     const int j0 = t * BC;
     // hidden-key bits of the tile (padding, keys past s_k); wave-uniform
     uint64_t hid;
@@ -413,18 +430,23 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     load_half(0);
     store_half(0);
     load_half(1);
+    store_half(1);
+    load_half(2);
   }
   __syncthreads();
 
   // ---- ping-pong phases (2 * n_kv + 2, each closed by a barrier). Group 0
   // runs  M(0) V(0) M(1) V(1) ... V(n-1) M(n),  group 1 the same one phase
-  // later, where M(t) = [PV(t-1), QK(t), staging] issues the matrix-core work
-  // (plus LDS stores and global loads, which fit between its MFMAs) and
-  // V(t) = the softmax of S(t) runs on the vector ALU. Waves w and w + 4
-  // share a SIMD, so every SIMD holds one wave in an M step and one in a V
-  // step and the two units overlap. Tile u is written by group 0 in phase
-  // 2u - 2 and group 1 in phase 2u - 1, and read in phases 2u .. 2u + 3:
-  // three LDS buffers.
+  // later, where M(t) = [PV(t-1), QK(t), V staging] issues the matrix-core
+  // work and V(t) = [K staging, softmax of S(t)] the vector-ALU work. Waves w
+  // and w + 4 share a SIMD, so every SIMD holds one wave in an M step and one
+  // in a V step and the two units overlap. The staging is split between the
+  // two kinds of step so that they take about equally long. LDS buffer
+  // u % 4 holds tile u: its K half is written in phases 2u - 3 (group 0) and
+  // 2u - 2 (group 1) and read by QK(u) in phases 2u, 2u + 1; its V half is
+  // written in phases 2u - 2, 2u - 1 and read by PV(u) in phases 2u + 1 ..
+  // 2u + 3 (from the prefetch at the end of V(u) on). Both halves are free
+  // again before tile u + 4 is written, from phase 2u + 5 on.
   // Phase boundary. The barrier orders memory only; the scheduling fences on
   // both sides also keep register-only work in its phase (otherwise the
   // compiler sinks the softmax into the next M step to fill MFMA gaps, and
@@ -434,22 +456,31 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
+  // Phase boundary after V(t): the step's LDS writes are completed and
+  // published (release), then the first LA fragments of PV(t) are requested,
+  // and their latency overlaps the barrier wait. V tile t is not written
+  // again before PV(t) has read it.
+  auto vstep_sync = [&](int t) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+#pragma unroll
+    for (int i = 0; i < LA; ++i) vpre[i] = v_frag(t, i);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_sched_barrier(0);
+  };
   if (grp == 0) {
-    if (n_kv > 0) {
-      qk(0);
-      store_half(1);
-      load_half(2);
-    }
+    if (n_kv > 0) qk(0);
     phase_sync();
     for (int t = 0; t < n_kv - 1; ++t) {
       vstep(t);
-      phase_sync();
+      vstep_sync(t);
       m_step(t, t + 1);
       phase_sync();
     }
     if (n_kv > 0) {
       vstep(n_kv - 1);
-      phase_sync();
+      vstep_sync(n_kv - 1);
       pv(n_kv - 1);
       phase_sync();
     }
@@ -458,17 +489,15 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     phase_sync();  // phase 0: group 0 alone
     if (n_kv > 0) {
       qk(0);
-      store_half(1);
-      load_half(2);
       phase_sync();
       vstep(0);
-      phase_sync();
+      vstep_sync(0);
     }
     for (int t = 1; t < n_kv; ++t) {
       m_step(t - 1, t);
       phase_sync();
       vstep(t);
-      phase_sync();
+      vstep_sync(t);
     }
     if (n_kv > 0) pv(n_kv - 1);
     phase_sync();
