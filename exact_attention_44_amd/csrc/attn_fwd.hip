@@ -360,7 +360,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     // exp2 sum shows a score more than ~20 (log2 units) above it, i.e. the
     // sum exceeds 2^20 or overflows; then O and l are rescaled and the tile
     // is recomputed. O / l is the same for any reference.
-    if (__ballot(m_run == -INFINITY) != 0ull) {
+    // Without a padding mask every row sees key 0, so tile 0 is every row's
+    // first visible tile and the test needs no vote.
+    if (PADMASK ? (__ballot(m_run == -INFINITY) != 0ull) : (t == 0)) {
       float mx = sc[0][0];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -411,7 +413,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      // a lane whose row has no visible key yet keeps O = l = 0 and the
+      // neutral reference (the branch is taken by the whole wave)
+      const bool none = m_new == -INFINITY;
+      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
         }
       l_run *= alpha;
       m_run = m_new;
-      nmc = -m_new * c;
+      nmc = none ? 0.f : -m_new * c;
       rs = weights();
     }
     l_run += rs;
