@@ -95,6 +95,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)n, 0x00020000);
 }
 
+// 16 bytes per lane from the buffer straight into LDS: lane i's bytes land at
+// dst + 16 i (dst is wave-uniform). A device function of its own, so the host
+// compilation pass never sees the LDS address-space cast.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, byte_off, 0,
+                                          0, 0);
+}
+
 __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
@@ -116,11 +124,20 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int K_BYTES = BC * KS;
   constexpr int BUF_BYTES = K_BYTES + D * VS;
   constexpr int NBUF = 4;             // see the phase schedule below
-  // Each group stages its half (32 keys) of a tile: K in 16-byte pieces, V in
-  // items of 2 keys x 8 columns (transposed on the way into LDS).
+  // Each group stages its half (32 keys) of a tile. K goes from memory
+  // straight into its padded LDS rows (buffer loads with LDS as the
+  // destination): the half is 32 rows of ROW_SLOTS 16-byte slots, written by
+  // K_DMA instructions of 64 consecutive slots each; the last instruction
+  // overlaps its predecessor, so the overlap is written twice with the same
+  // data, and a padding slot receives its row's first 16 bytes. V goes
+  // through registers in items of 2 keys x 8 columns, transposed on the way
+  // into LDS.
   constexpr int GT = NT / 2;
-  constexpr int K_LD = 32 * KU / GT;
-  static_assert((32 * KU) % GT == 0, "K half tile must split evenly over a group");
+  constexpr int ROW_SLOTS = KS / 16;
+  constexpr int K_SLOTS = 32 * ROW_SLOTS;
+  constexpr int K_DMA = (K_SLOTS + 63) / 64;
+  constexpr int K_DMA_W = (K_DMA + 3) / 4;  // per wave, at most
+  static_assert(K_SLOTS >= 64, "a half tile must fill one DMA instruction");
   constexpr int V_ITEMS = 16 * (D / 8);
   constexpr int V_LD = (V_ITEMS + GT - 1) / GT;
   constexpr float kSumLimit = 1048576.f;  // 2^20: see the softmax phase
@@ -193,19 +210,31 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   }
 
   // ---- staging of this group's half (keys 32*grp .. 32*grp+31) of a tile
-  u32x4_t kr[K_LD];
-  u32x4_t vr[V_LD][2];
-  auto load_k = [&](int u) {
+  const int wg = wv & 3;  // wave within its group
+  uint32_t k_voff[K_DMA_W];
+#pragma unroll
+  for (int i = 0; i < K_DMA_W; ++i) {
+    const int j = wg + 4 * i;
+    const int slot = min(64 * j, K_SLOTS - 64) + lane;
+    const int row = 32 * grp + slot / ROW_SLOTS, un = slot % ROW_SLOTS;
+    k_voff[i] = (uint32_t)(row * D + (un < KU ? 8 * un : 0)) * 2;
+  }
+  // K rows of tile u into LDS; completes asynchronously (the next fenced
+  // barrier of this wave waits for it).
+  auto dma_k = [&](int u) {
     const int j0 = u * BC;
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D * 2;
     const __amdgpu_buffer_rsrc_t rkt = make_rsrc(kg + (int64_t)j0 * D, rest);
+    char* kl = lds + (u % NBUF) * BUF_BYTES + grp * K_SLOTS * 16;
 #pragma unroll
-    for (int i = 0; i < K_LD; ++i) {
-      const int id = i * GT + gt;
-      const int row = 32 * grp + id / KU, un = id % KU;
-      kr[i] = load16(rkt, (uint32_t)(row * D + 8 * un) * 2);
+    for (int i = 0; i < K_DMA_W; ++i) {
+      const int j = wg + 4 * i;
+      if (j < K_DMA) {
+        load16_to_lds(rkt, kl + min(64 * j, K_SLOTS - 64) * 16, k_voff[i]);
+      }
     }
   };
+  u32x4_t vr[V_LD][2];
   auto load_v = [&](int u) {
     const int j0 = u * BC;
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D * 2;
@@ -219,15 +248,6 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) vr[i][r] = load16(rvt, (uint32_t)((key + r) * D + 8 * dc) * 2);
       }
-    }
-  };
-  auto store_k = [&](int u) {
-    char* kl = lds + (u % NBUF) * BUF_BYTES;
-#pragma unroll
-    for (int i = 0; i < K_LD; ++i) {
-      const int id = i * GT + gt;
-      const int row = 32 * grp + id / KU, un = id % KU;
-      *(u32x4_t*)(kl + row * KS + un * 16) = kr[i];
     }
   };
   auto store_v = [&](int u) {
@@ -246,8 +266,6 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       }
     }
   };
-  auto load_half = [&](int u) { load_k(u); load_v(u); };
-  auto store_half = [&](int u) { store_k(u); store_v(u); };
 
   // ---- per-wave running state: O^T (one query per lane), row max, row sum
   f32x16_t o[DB];
@@ -331,8 +349,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   };
   // V step: masks and online softmax of S(t) -> P(t).
   auto vstep = [&](int t) {
-    store_k(t + 2);
-    load_k(t + 3);
+    dma_k(t + 3);
     const int j0 = t * BC;
     // hidden-key bits of the tile (padding, keys past s_k); wave-uniform
     uint64_t hid;
@@ -432,11 +449,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   };
 
   if (n_kv > 0) {
-    load_half(0);
-    store_half(0);
-    load_half(1);
-    store_half(1);
-    load_half(2);
+    dma_k(0);
+    dma_k(1);
+    dma_k(2);
+    load_v(0);
+    store_v(0);
+    load_v(1);
+    store_v(1);
+    load_v(2);
   }
   __syncthreads();
 
@@ -461,17 +481,19 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Phase boundary after V(t): the step's LDS writes are completed and
-  // published (release), then the first LA fragments of PV(t) are requested,
-  // and their latency overlaps the barrier wait. V tile t is not written
-  // again before PV(t) has read it.
+  // Phase boundary after V(t). The V step writes no LDS through its own
+  // stores (its K tile arrives by DMA, which the fenced barrier at the end of
+  // the next M step waits for, long before the tile is read), so this barrier
+  // needs no memory fence; the first LA fragments of PV(t) are requested
+  // right before it, and their latency overlaps the barrier wait. V tile t is
+  // not written again before PV(t) has read it.
   auto vstep_sync = [&](int t) {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
 #pragma unroll
     for (int i = 0; i < LA; ++i) vpre[i] = v_frag(t, i);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
   };
   if (grp == 0) {

@@ -42,6 +42,13 @@ def test_exports_every_declared_function(lib):
         assert re.search(rf"\bT {n}\b", dyn), f"{n} not exported"
 
 
+def test_every_kernel_has_its_host_launch_stub():
+    # a kernel whose body the host compilation pass rejects loses its launch
+    # stub without a build error; the library then fails to load
+    und = subprocess.run(["nm", "-C", "--undefined-only", LIB_PATH], capture_output=True, text=True).stdout
+    assert "__device_stub__" not in und, und
+
+
 def test_library_never_allocates_device_memory():
     und = subprocess.run(["nm", "-D", "--undefined-only", LIB_PATH], capture_output=True, text=True).stdout
     assert "hipMalloc" not in und and "hipFree" not in und and "hipHostMalloc" not in und
