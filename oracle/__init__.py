@@ -5,6 +5,7 @@ from .attention import (  # noqa: F401
     attention_online_fp64,
     attention_rows_fp64,
     attention_weights_fp64,
+    merge_partials_fp64,
     score_matrix_bytes,
     score_matrix_gb,
 )

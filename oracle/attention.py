@@ -33,6 +33,9 @@ Functions:
                             with running softmax statistics (a second,
                             independent CPU path used to pin the first);
   attention_bruteforce      pure-Python loops with math.exp / math.fsum;
+  merge_partials_fp64       combination of results over disjoint key sets
+                            into the result over their union (for the key-
+                            split forward);
   score_matrix_bytes / score_matrix_gb
                             the closed form of the materialised score memory.
 """
@@ -51,6 +54,7 @@ __all__ = [
     "attention_weights_fp64",
     "attention_online_fp64",
     "attention_bruteforce",
+    "merge_partials_fp64",
 ]
 
 NEG_INF = -np.inf
@@ -286,4 +290,41 @@ def attention_bruteforce(q, k, v, scale: float, causal: bool = False,
                 for c in range(d):
                     O[b, h, i, c] = math.fsum(e * float(v[b, h, j, c]) for j, e in w) / tot
                 lse[b, h, i] = mx + math.log(tot)
+    return O, lse
+
+
+# ----------------------------------------------------------------------------
+# Results over disjoint key sets -> result over their union.
+# The news.hamidun.com glossary entry "Flash attention" (fourth paragraph)
+# names inference frameworks and Ring Attention, which partitions the method's
+# work over keys across devices; the pages give no formula for recombining the
+# parts. It follows from the definition above (onecalc.app "Attention memory",
+# section "What this memory is"): for key sets K_1..K_Z that partition the
+# visible keys of row i, the row's exp-sum over the union is the sum of the
+# per-set sums, L = sum_z exp(lse_z) (each lse_z = M_z + ln L_z, against any
+# common reference), and the union's weighted value sum is the sum of the
+# per-set ones, sum_z L_z O_z. Hence lse = ln sum_z exp(lse_z) and
+# O = sum_z exp(lse_z - lse) O_z. A set in which the row sees no key has
+# lse_z = -inf and weight 0; a row that sees no key in any set gets O = 0 and
+# lse = -inf, as in the definition.
+# ----------------------------------------------------------------------------
+def merge_partials_fp64(outs, lses) -> Tuple[np.ndarray, np.ndarray]:
+    """outs: [Z, ..., d] per-set outputs; lses: [Z, ...] per-set log-sum-exps.
+
+    Returns (O, lse) of the union, float64.
+    """
+    outs = _as_f64(outs)
+    lses = _as_f64(lses)
+    if outs.shape[:-1] != lses.shape:
+        raise ValueError("outs must be lses.shape + (d,)")
+    M = lses.max(axis=0)                     # a common reference per row
+    empty = np.isneginf(M)
+    M_safe = np.where(empty, 0.0, M)
+    w = np.exp(lses - M_safe[None])          # exp(-inf) == 0 for empty sets
+    total = w.sum(axis=0)
+    lse = np.full(M.shape, NEG_INF)
+    lse[~empty] = M[~empty] + np.log(total[~empty])
+    frac = np.zeros_like(w)
+    frac[:, ~empty] = w[:, ~empty] / total[None, ~empty]
+    O = (frac[..., None] * outs).sum(axis=0)
     return O, lse

@@ -298,6 +298,47 @@ def pin_fully_masked_rows():
     assert O.shape == (1, 2, 3, 4) and np.all(O == 0.0) and np.all(np.isneginf(lse))
 
 
+def chunk_partials(c, bounds):
+    """The oracle on each key chunk [lo, hi) alone (keys outside it padded)."""
+    B, s_k = c["q"].shape[0], c["k"].shape[2]
+    outs, lses = [], []
+    for lo, hi in bounds:
+        outside = np.ones(s_k, bool)
+        outside[lo:hi] = False
+        kpm = np.broadcast_to(outside, (B, s_k)).astype(np.uint8)
+        if c["kpm"] is not None:
+            kpm = kpm | c["kpm"]
+        O, lse = A.attention_fp64(c["q"], c["k"], c["v"], c["scale"], c["causal"], kpm)
+        outs.append(O)
+        lses.append(lse)
+    return np.stack(outs), np.stack(lses)
+
+
+def pin_merge_of_key_chunks():
+    """Merging the definition's results over key chunks gives the definition
+    over all keys (softmax over a union of disjoint key sets), for chunkings
+    with empty chunks, single keys, and chunks some rows see nothing of."""
+    for seed, causal, mask in ((121, False, "none"), (122, True, "none"), (123, True, "lengths"),
+                               (124, False, "random"), (125, True, "all")):
+        c = f64_case(seed, 2, 2, 23, 37, 8, causal=causal, mask=mask)
+        O, lse = run(c)
+        for bounds in ([(0, 37)], [(0, 10), (10, 37)], [(0, 5), (5, 6), (6, 30), (30, 37)],
+                       [(0, 0), (0, 37), (37, 37)]):
+            outs, lses = chunk_partials(c, bounds)
+            Om, lm = A.merge_partials_fp64(outs, lses)
+            close(Om, O, 1e-13, f"merged O seed={seed} chunks={bounds}")
+            close(lm, lse, 1e-13, f"merged lse seed={seed} chunks={bounds}")
+    # closed forms: two parts with equal lse average, and the lse gains ln 2;
+    # a part with lse -inf has no weight
+    o1, o2 = np.array([[1.0, -2.0]]), np.array([[3.0, 4.0]])
+    Om, lm = A.merge_partials_fp64(np.stack([o1, o2]), np.array([[0.7], [0.7]]))
+    close(Om, (o1 + o2) / 2, 1e-15, "equal halves")
+    close(lm, np.array([0.7 + np.log(2.0)]), 1e-15, "equal halves lse")
+    Om, lm = A.merge_partials_fp64(np.stack([o1, o2]), np.array([[-np.inf], [1.5]]))
+    close(Om, o2, 1e-15, "empty part")
+    close(lm, np.array([1.5]), 1e-15, "empty part lse")
+
+
 PINS = [
     pin_worked_example,
     pin_oracle_materialises_closed_form,
@@ -311,4 +352,5 @@ PINS = [
     pin_invariances,
     pin_large_scores,
     pin_fully_masked_rows,
+    pin_merge_of_key_chunks,
 ]

@@ -95,3 +95,46 @@ def test_mutant_is_caught(name, monkeypatch):
         except Exception as e:  # AssertionError or a shape error both mean "caught"
             failed.append((pin.__name__, type(e).__name__))
     assert failed, f"mutant {name} passed every pin"
+
+
+def _merge_plain_average(outs, lses):
+    O, lse = ORIG_MERGE(outs, lses)
+    return np.asarray(outs).mean(axis=0), lse
+
+
+def _merge_lse_is_max(outs, lses):
+    O, lse = ORIG_MERGE(outs, lses)
+    return O, np.asarray(lses).max(axis=0)
+
+
+def _merge_unnormalised(outs, lses):
+    lses = np.asarray(lses)
+    w = np.exp(np.where(np.isneginf(lses), -np.inf, lses))
+    O = (w[..., None] * np.asarray(outs)).sum(axis=0)
+    return O, ORIG_MERGE(outs, lses)[1]
+
+
+def _merge_weights_reversed(outs, lses):
+    return ORIG_MERGE(np.asarray(outs)[::-1], lses)
+
+
+ORIG_MERGE = A.merge_partials_fp64
+MERGE_MUTANTS = {
+    "merge_plain_average": _merge_plain_average,
+    "merge_lse_is_max": _merge_lse_is_max,
+    "merge_unnormalised": _merge_unnormalised,
+    "merge_weights_reversed": _merge_weights_reversed,
+}
+
+
+@pytest.mark.parametrize("name", sorted(MERGE_MUTANTS))
+def test_merge_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(A, "merge_partials_fp64", MERGE_MUTANTS[name])
+    failed = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception as e:
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"
