@@ -18,7 +18,10 @@ memory). Prints one JSON line:
 Before the W warm-up steps, --ramp-ms (default 100) of untimed back-to-back
 steps bring the GPU to its sustained clock; the timed region is exactly K
 steps. Options: --workload i selects another of the five workloads (for sweeps; the
-default line is the s = 8192 one); --calibrate-copy adds one plain device copy
+default line is the s = 8192 one); --split-workload i --splits n times the
+key-split entry point (attn_fwd_split: n key chunks, then their merge) on a
+shape from workloads.SPLIT_WORKLOADS; a workload with key padding also reports
+useful_tflops (FLOPs on the visible keys only); --calibrate-copy adds one plain device copy
 of known size after the timed region, so a counter profile of this command also
 holds the reference that scales FETCH_SIZE / WRITE_SIZE to bytes.
 """
@@ -61,6 +64,11 @@ def parse():
                     help="untimed back-to-back steps before the warm-up steps, so the "
                          "GPU reaches its sustained clock (it needs ~25 ms of load)")
     ap.add_argument("--workload", type=int, default=2, help="index into workloads.WORKLOADS")
+    ap.add_argument("--split-workload", type=int, default=None,
+                    help="index into workloads.SPLIT_WORKLOADS: time the key-split entry point "
+                         "(attn_fwd_split) on that shape instead")
+    ap.add_argument("--splits", type=int, default=4,
+                    help="key chunks for --split-workload (1 = the plain launch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -122,10 +130,11 @@ def main():
     import torch
 
     import exact_attention_44_amd as E
-    from workloads import WORKLOADS
+    from workloads import SPLIT_WORKLOADS, WORKLOADS
 
     E.load_library()
-    w = WORKLOADS[a.workload]
+    split = a.split_workload is not None
+    w = SPLIT_WORKLOADS[a.split_workload] if split else WORKLOADS[a.workload]
     from workloads import generate
     g = generate(w)
     dev = torch.device("cuda:0")
@@ -138,10 +147,20 @@ def main():
     args = (q, k, v, out, lse, w.B, w.H, w.s_q, w.s_k, w.d, float(g["scale"]), w.causal, kpm,
             stream.cuda_stream)
 
-    def step():
-        st = E.attn_fwd(*args)
-        if st != E.ATTN_OK:
-            raise E.AttnError(st)
+    if split:
+        chunks = max(1, min(a.splits, (w.s_k + 63) // 64))
+        ws_bytes = E.attn_fwd_split_workspace_bytes(w.B, w.H, w.s_q, w.d, chunks)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # outside the timed region
+
+        def step():
+            st = E.attn_fwd_split(*args[:13], a.splits, ws, ws_bytes, args[13])
+            if st != E.ATTN_OK:
+                raise E.AttnError(st)
+    else:
+        def step():
+            st = E.attn_fwd(*args)
+            if st != E.ATTN_OK:
+                raise E.AttnError(st)
 
     t_ramp = time.perf_counter()
     ramp_steps = 0
@@ -216,11 +235,20 @@ def main():
             "traffic": traffic,
             "traffic_unit": "bytes per launch",
             "traffic_detail": traffic_detail,
-            "kernel": "attn_fwd_kernel",
+            "kernel": ("attn_fwd_kernel (key-split) + attn_merge_kernel" if split
+                       else "attn_fwd_kernel"),
             "kernel_avg_ms": round(kern_avg_ms, 5),
             "kernel_min_ms": round(min(kern_ms), 5),
         },
     }
+    if split:
+        res["config"]["n_splits"] = a.splits
+        res["config"]["entry_point"] = "attn_fwd_split"
+    if w.padded:
+        # the metric's nominal FLOPs ignore padding; the work on visible keys only
+        lengths = g["lengths"]
+        useful = sum(4.0 * w.H * w.s_q * int(n) * w.d for n in lengths)
+        res["useful_tflops"] = round(useful * a.steps / wall / 1e12, 2)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, g, a.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -15,9 +15,10 @@ from .build import LIB_PATH
 
 __all__ = [
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
-    "ATTN_ERR_ALIAS", "ATTN_ERR_SCALE", "ATTN_ERR_LAUNCH", "AttnError", "load_library",
-    "attn_fwd", "attn_fwd_validate", "attn_status_str", "attn_last_hip_error", "fwd",
-    "LIB_PATH",
+    "ATTN_ERR_ALIAS", "ATTN_ERR_SCALE", "ATTN_ERR_LAUNCH", "ATTN_ERR_WORKSPACE", "AttnError",
+    "load_library", "attn_fwd", "attn_fwd_validate", "attn_fwd_split",
+    "attn_fwd_split_workspace_bytes", "attn_status_str", "attn_last_hip_error", "fwd",
+    "fwd_split", "LIB_PATH",
 ]
 
 ATTN_OK = 0
@@ -28,6 +29,7 @@ ATTN_ERR_ALIGN = 4
 ATTN_ERR_ALIAS = 5
 ATTN_ERR_SCALE = 6
 ATTN_ERR_LAUNCH = 7
+ATTN_ERR_WORKSPACE = 8
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -64,6 +66,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_validate.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                       ctypes.c_float, ctypes.c_int, vp]
     lib.attn_fwd_validate.restype = ctypes.c_int
+    lib.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                   ctypes.c_float, ctypes.c_int, vp, i64, vp, i64, vp]
+    lib.attn_fwd_split.restype = ctypes.c_int
+    lib.attn_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.attn_fwd_split_workspace_bytes.restype = i64
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -97,6 +104,20 @@ def attn_fwd_validate(q, k, v, out, lse, B: int, H: int, s_q: int, s_k: int, d: 
                                             1 if causal else 0, _ptr(key_padding_mask))
 
 
+def attn_fwd_split(q, k, v, out, lse, B: int, H: int, s_q: int, s_k: int, d: int, scale: float,
+                   causal: bool, key_padding_mask, n_splits: int, workspace, workspace_bytes: int,
+                   stream) -> int:
+    """The C entry point attn_fwd_split with the same arguments."""
+    return load_library().attn_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                         B, H, s_q, s_k, d, float(scale), 1 if causal else 0,
+                                         _ptr(key_padding_mask), n_splits, _ptr(workspace),
+                                         workspace_bytes, stream)
+
+
+def attn_fwd_split_workspace_bytes(B: int, H: int, s_q: int, d: int, n_splits: int) -> int:
+    return load_library().attn_fwd_split_workspace_bytes(B, H, s_q, d, n_splits)
+
+
 def attn_status_str(status: int) -> str:
     return load_library().attn_status_str(status).decode()
 
@@ -105,12 +126,7 @@ def attn_last_hip_error() -> int:
     return load_library().attn_last_hip_error()
 
 
-def fwd(q, k, v, *, causal: bool = False, key_padding_mask=None, scale: Optional[float] = None,
-        out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
-    """Attention forward on torch device tensors: q [B,H,s_q,d], k/v [B,H,s_k,d]
-    bf16 contiguous; key_padding_mask None or uint8/bool [B,s_k] (nonzero =
-    padded). Returns (out bf16 [B,H,s_q,d], lse float32 [B,H,s_q]). Runs on
-    torch's current stream of q's device."""
+def _check_inputs(q, k, v, key_padding_mask):
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -128,6 +144,18 @@ def fwd(q, k, v, *, causal: bool = False, key_padding_mask=None, scale: Optional
             raise ValueError("key_padding_mask must be uint8/bool [B, s_k]")
         if not m.is_cuda or not m.is_contiguous():
             raise ValueError("key_padding_mask must be a contiguous device tensor")
+    return B, H, s_q, s_k, d
+
+
+def fwd(q, k, v, *, causal: bool = False, key_padding_mask=None, scale: Optional[float] = None,
+        out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Attention forward on torch device tensors: q [B,H,s_q,d], k/v [B,H,s_k,d]
+    bf16 contiguous; key_padding_mask None or uint8/bool [B,s_k] (nonzero =
+    padded). Returns (out bf16 [B,H,s_q,d], lse float32 [B,H,s_q]). Runs on
+    torch's current stream of q's device."""
+    import torch
+
+    B, H, s_q, s_k, d = _check_inputs(q, k, v, key_padding_mask)
     if scale is None:
         scale = d ** -0.5
     with torch.cuda.device(q.device):
@@ -137,6 +165,38 @@ def fwd(q, k, v, *, causal: bool = False, key_padding_mask=None, scale: Optional
             lse = torch.empty((B, H, s_q), dtype=torch.float32, device=q.device)
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = attn_fwd(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal, key_padding_mask, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, lse
+
+
+def fwd_split(q, k, v, *, n_splits: int, causal: bool = False, key_padding_mask=None,
+              scale: Optional[float] = None, out=None, lse=None,
+              workspace=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """As fwd, computed over n_splits key chunks merged through their
+    log-sum-exps (attn_fwd_split). `workspace` is an optional device tensor of
+    at least attn_fwd_split_workspace_bytes(...) bytes, 256-byte aligned; when
+    None, one is allocated with torch for this call."""
+    import torch
+
+    B, H, s_q, s_k, d = _check_inputs(q, k, v, key_padding_mask)
+    if scale is None:
+        scale = d ** -0.5
+    chunks = max(1, min(int(n_splits), (s_k + 63) // 64))
+    need = attn_fwd_split_workspace_bytes(B, H, s_q, d, chunks)
+    if need < 0:
+        raise AttnError(ATTN_ERR_SHAPE)
+    with torch.cuda.device(q.device):
+        if out is None:
+            out = torch.empty((B, H, s_q, d), dtype=torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, H, s_q), dtype=torch.float32, device=q.device)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_fwd_split(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
+                            key_padding_mask, int(n_splits), workspace, ws_bytes, stream)
     if st != ATTN_OK:
         raise AttnError(st)
     return out, lse

@@ -49,6 +49,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -61,6 +62,9 @@ struct FwdParams {
   float* lse;
   const uint8_t* kpm;
   int s_q, s_k, H, BH, n_qt;
+  int k_chunk;      // keys per chunk of a key-split launch (a multiple of 64)
+  float* o_part;    // key-split partial outputs, fp32 [chunk][B*H][s_q][d]
+  float* lse_part;  // key-split partial log-sum-exps, fp32 [chunk][B*H][s_q]
   float c;          // |scale| * log2(e): scores enter exp2 as s * c
   float scale_abs;  // |scale|, for the log-sum-exp output
   uint32_t q_xor;   // 0x80008000 when scale < 0: Q negated, so c stays > 0
@@ -107,7 +111,7 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t byt
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
 
-template <int D, bool CAUSAL, bool PADMASK>
+template <int D, bool CAUSAL, bool PADMASK, bool SPLIT>
 __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int NT = 512;             // 8 waves: two ping-pong groups of 4
   constexpr int BR = 256;             // query rows per workgroup, 32 per wave
@@ -159,21 +163,25 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   const int b = bh / p.H;
   const int q0 = qt * BR;
   const int s_q = p.s_q, s_k = p.s_k;
+  // Key range of this workgroup: all keys, or chunk blockIdx.y of a key-split
+  // launch. Key indices below are relative to k0; s_kc keys are in range.
+  const int k0 = SPLIT ? (int)blockIdx.y * p.k_chunk : 0;
+  const int s_kc = SPLIT ? max(0, min(s_k, k0 + p.k_chunk) - k0) : s_k;
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (int64_t)bh * s_q * D, (uint32_t)s_q * D * 2);
-  const uint16_t* kg = p.k + (int64_t)bh * s_k * D;
-  const uint16_t* vg = p.v + (int64_t)bh * s_k * D;
-  const uint8_t* mg = PADMASK ? p.kpm + (int64_t)b * s_k : nullptr;
+  const uint16_t* kg = p.k + ((int64_t)bh * s_k + k0) * D;
+  const uint16_t* vg = p.v + ((int64_t)bh * s_k + k0) * D;
+  const uint8_t* mg = PADMASK ? p.kpm + (int64_t)b * s_k + k0 : nullptr;
 
   // ---- keys this tile can see: causal stops at the last query row; padding
   // stops after the last key that is not padded.
-  int kend = s_k;
-  if (CAUSAL) kend = min(kend, q0 + BR);
+  int kend = s_kc;
+  if (CAUSAL) kend = min(kend, q0 + BR - k0);
   if (PADMASK) {
     if (tid == 0) lds_last = -1;
     __syncthreads();
     int last = -1;
-    for (int cend = s_k; cend > 0; cend -= NT * 4) {
+    for (int cend = s_kc; cend > 0; cend -= NT * 4) {
       const int cbeg = max(0, cend - NT * 4);
       int best = -1;
 #pragma unroll
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     }
     kend = min(kend, last + 1);
   }
-  const int n_kv = (kend + BC - 1) / BC;
+  const int n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
 
   // ---- Q fragments (B operand of the score product), kept in registers.
   const int qlo = q0 + 32 * wv;  // first query row of this wave
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // barrier of this wave waits for it).
   auto dma_k = [&](int u) {
     const int j0 = u * BC;
-    const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D * 2;
+    const uint32_t rest = (uint32_t)max(s_kc - j0, 0) * D * 2;
     const __amdgpu_buffer_rsrc_t rkt = make_rsrc(kg + (int64_t)j0 * D, rest);
     char* kl = lds + (u % NBUF) * BUF_BYTES + grp * K_SLOTS * 16;
 #pragma unroll
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   u32x4_t vr[V_LD][2];
   auto load_v = [&](int u) {
     const int j0 = u * BC;
-    const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D * 2;
+    const uint32_t rest = (uint32_t)max(s_kc - j0, 0) * D * 2;
     const __amdgpu_buffer_rsrc_t rvt = make_rsrc(vg + (int64_t)j0 * D, rest);
 #pragma unroll
     for (int i = 0; i < V_LD; ++i) {
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     }
     if (PADMASK) {
       const int key = t * BC + lane;
-      mbyte = key < s_k ? (uint32_t)mg[key] : 1u;
+      mbyte = key < s_kc ? (uint32_t)mg[key] : 1u;
     }
   };
   // One M step: value product of tile tp, then score product of tile tq,
@@ -356,11 +364,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     if (PADMASK) {
       hid = __ballot(mbyte != 0u);
     } else {
-      const int rem = s_k - j0;
+      const int rem = s_kc - j0;
       hid = rem >= BC ? 0ull : ~((1ull << rem) - 1ull);
     }
-    if (hid != 0ull || (CAUSAL && j0 + BC - 1 > qlo)) {
-      const int lim = qlo + ln - j0;  // causal: key offset visible iff <= lim
+    if (hid != 0ull || (CAUSAL && k0 + j0 + BC - 1 > qlo)) {
+      const int lim = qlo + ln - k0 - j0;  // causal: key offset visible iff <= lim
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const uint32_t sh = (uint32_t)(hid >> (32 * kb)) >> (8 * hl);
@@ -534,7 +542,25 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
   const int row = qlo + ln;
-  if (row < s_q) {
+  if (SPLIT && row < s_q) {
+    // partial result of this key chunk: fp32 O / l and its log-sum-exp
+    const int64_t pr = ((int64_t)blockIdx.y * p.BH + bh) * s_q + row;
+    float* op = p.o_part + pr * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = o[db][4 * g + e] * inv;
+        *(f32x4_t*)(op + 32 * db + 8 * g + 4 * hl) = w;
+      }
+    }
+    if (hl == 0) {
+      p.lse_part[pr] = l_tot > 0.f ? m_run * p.scale_abs + __builtin_amdgcn_logf(l_tot) * kLn2
+                                   : -INFINITY;
+    }
+  } else if (row < s_q) {
     uint16_t* og = p.out + ((int64_t)bh * s_q + row) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -563,10 +589,80 @@ constexpr int rows_per_block() {
 
 thread_local int g_last_hip_error = 0;
 
-template <int D, bool CAUSAL, bool PADMASK>
-hipError_t launch(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, PADMASK>), dim3(grid), dim3(512), 0, stream, p);
+template <int D, bool CAUSAL, bool PADMASK, bool SPLIT>
+hipError_t launch(const FwdParams& p, int grid, int chunks, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, PADMASK, SPLIT>), dim3(grid, chunks), dim3(512), 0,
+                     stream, p);
   return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t launch_fwd(const FwdParams& p, int64_t d, bool causal, bool pad, int grid, int chunks,
+                      hipStream_t hs) {
+  if (d == 128) {
+    if (causal)
+      return pad ? launch<128, true, true, SPLIT>(p, grid, chunks, hs)
+                 : launch<128, true, false, SPLIT>(p, grid, chunks, hs);
+    return pad ? launch<128, false, true, SPLIT>(p, grid, chunks, hs)
+               : launch<128, false, false, SPLIT>(p, grid, chunks, hs);
+  }
+  if (causal)
+    return pad ? launch<64, true, true, SPLIT>(p, grid, chunks, hs)
+               : launch<64, true, false, SPLIT>(p, grid, chunks, hs);
+  return pad ? launch<64, false, true, SPLIT>(p, grid, chunks, hs)
+             : launch<64, false, false, SPLIT>(p, grid, chunks, hs);
+}
+
+// Merge of the key-split partial results (one wave per query row): with
+// per-chunk log-sum-exps lse_z and outputs O_z (each normalised by its own
+// row sum), lse = ln sum_z exp(lse_z) and O = sum_z exp(lse_z - lse) O_z.
+// This is the softmax over the union of the chunks' keys (the weights of
+// chunk z are its own weights times exp(lse_z - lse)). A row that sees no key
+// in any chunk gets O = 0 and lse = -inf. Memory-bound: it reads the
+// partials once.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ o_part,
+                                                         const float* __restrict__ lse_part,
+                                                         uint16_t* __restrict__ out,
+                                                         float* __restrict__ lse, int64_t rows,
+                                                         int chunks) {
+  constexpr int E = D / 64;  // output elements per lane
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;  // the whole wave leaves together
+  float m = -INFINITY;
+  for (int z = lane; z < chunks; z += 64) m = fmaxf(m, lse_part[(int64_t)z * rows + row]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  uint16_t* orow = out + row * D + lane * E;
+  if (m == -INFINITY) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) orow[e] = 0;
+    if (lane == 0) lse[row] = -INFINITY;
+    return;
+  }
+  float s = 0.f;
+  for (int z = lane; z < chunks; z += 64)
+    s += __builtin_amdgcn_exp2f((lse_part[(int64_t)z * rows + row] - m) * kLog2e);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  const float L = m + __builtin_amdgcn_logf(s) * kLn2;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int z = 0; z < chunks; ++z) {
+    const float w = __builtin_amdgcn_exp2f((lse_part[(int64_t)z * rows + row] - L) * kLog2e);
+    const float* op = o_part + ((int64_t)z * rows + row) * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(w, op[e], acc[e]);
+  }
+  if (E == 2) {
+    *(uint32_t*)orow = pack_bf16(acc[0], acc[E - 1]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) orow[e] = (uint16_t)(pack_bf16(acc[e], 0.f) & 0xFFFFu);
+  }
+  if (lane == 0) lse[row] = L;
 }
 
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -614,16 +710,12 @@ extern "C" int attn_fwd_validate(const void* q, const void* k, const void* v, co
   return ATTN_OK;
 }
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                        int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d, float scale,
-                        int causal, const uint8_t* key_padding_mask, void* stream) {
-  const int st = attn_fwd_validate(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
-                                   key_padding_mask);
-  if (st != ATTN_OK) return st;
-  const int64_t BH = B * H;
-  if (BH == 0 || s_q == 0) return ATTN_OK;
+namespace {
 
-  FwdParams p;
+FwdParams make_params(const void* q, const void* k, const void* v, void* out, float* lse,
+                      int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d, float scale,
+                      const uint8_t* key_padding_mask) {
+  FwdParams p = {};
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
@@ -633,7 +725,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   p.s_q = (int)s_q;
   p.s_k = (int)s_k;
   p.H = (int)H;
-  p.BH = (int)BH;
+  p.BH = (int)(B * H);
   const int64_t br = d == 128 ? rows_per_block<128>() : rows_per_block<64>();
   p.n_qt = (int)((s_q + br - 1) / br);
   const float sa = fabsf(scale);
@@ -648,27 +740,98 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
     p.c = sa * kLog2e;
     p.scale_abs = sa;
   }
-  const int grid = (int)blocks_for(BH, s_q, d);
-  const bool pad = key_padding_mask != nullptr && s_k > 0;
-  hipStream_t hs = (hipStream_t)stream;
-  hipError_t e;
-  if (d == 128) {
-    if (causal)
-      e = pad ? launch<128, true, true>(p, grid, hs) : launch<128, true, false>(p, grid, hs);
-    else
-      e = pad ? launch<128, false, true>(p, grid, hs) : launch<128, false, false>(p, grid, hs);
-  } else {
-    if (causal)
-      e = pad ? launch<64, true, true>(p, grid, hs) : launch<64, true, false>(p, grid, hs);
-    else
-      e = pad ? launch<64, false, true>(p, grid, hs) : launch<64, false, false>(p, grid, hs);
-  }
+  return p;
+}
+
+int finish(hipError_t e) {
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return ATTN_ERR_LAUNCH;
   }
   g_last_hip_error = 0;
   return ATTN_OK;
+}
+
+constexpr int64_t kMaxChunks = 65535;  // grid y limit
+
+// Keys per chunk for n chunks: a multiple of the 64-key tile.
+int64_t chunk_keys(int64_t s_k, int64_t n) {
+  const int64_t per = (s_k + n - 1) / n;
+  return ((per + 63) / 64) * 64;
+}
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d, float scale,
+                        int causal, const uint8_t* key_padding_mask, void* stream) {
+  const int st = attn_fwd_validate(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
+                                   key_padding_mask);
+  if (st != ATTN_OK) return st;
+  if (B * H == 0 || s_q == 0) return ATTN_OK;
+  const FwdParams p = make_params(q, k, v, out, lse, B, H, s_q, s_k, d, scale, key_padding_mask);
+  const int grid = (int)blocks_for(B * H, s_q, d);
+  const bool pad = key_padding_mask != nullptr && s_k > 0;
+  return finish(launch_fwd<false>(p, d, causal != 0, pad, grid, 1, (hipStream_t)stream));
+}
+
+extern "C" int64_t attn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t s_q, int64_t d,
+                                                  int64_t n_splits) {
+  if (B < 0 || H < 0 || s_q < 0 || (d != 64 && d != 128) || n_splits < 1 ||
+      n_splits > kMaxChunks)
+    return -1;
+  if (n_splits == 1) return 0;
+  const int64_t rows = B * H * s_q;
+  return align256(n_splits * rows * d * 4) + align256(n_splits * rows * 4);
+}
+
+extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d,
+                              float scale, int causal, const uint8_t* key_padding_mask,
+                              int64_t n_splits, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  int st = attn_fwd_validate(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
+                             key_padding_mask);
+  if (st != ATTN_OK) return st;
+  if (n_splits < 1 || n_splits > kMaxChunks) return ATTN_ERR_SHAPE;
+  // fewer chunks than 64-key tiles would leave chunks empty
+  const int64_t tiles = (s_k + 63) / 64;
+  const int64_t chunks = n_splits < tiles ? n_splits : (tiles > 0 ? tiles : 1);
+  if (chunks == 1) return attn_fwd(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
+                                   key_padding_mask, stream);
+  const int64_t need = attn_fwd_split_workspace_bytes(B, H, s_q, d, chunks);
+  if (B * H == 0 || s_q == 0) return ATTN_OK;
+  if (!workspace) return ATTN_ERR_NULL;
+  if ((uintptr_t)workspace & 255u) return ATTN_ERR_ALIGN;
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  const int64_t BH = B * H;
+  const int64_t nq = BH * s_q * d * 2, nk = BH * s_k * d * 2, nl = BH * s_q * 4;
+  const void* bufs[6] = {q, k, v, out, lse, key_padding_mask};
+  const int64_t sizes[6] = {nq, nk, nk, nq, nl, key_padding_mask ? B * s_k : 0};
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(workspace, need, bufs[i], sizes[i])) return ATTN_ERR_ALIAS;
+  if (((BH * s_q + 3) / 4) > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
+
+  FwdParams p = make_params(q, k, v, out, lse, B, H, s_q, s_k, d, scale, key_padding_mask);
+  p.k_chunk = (int)chunk_keys(s_k, chunks);
+  p.o_part = (float*)workspace;
+  p.lse_part = (float*)((char*)workspace + align256(chunks * BH * s_q * d * 4));
+  const int grid = (int)blocks_for(BH, s_q, d);
+  const bool pad = key_padding_mask != nullptr;
+  hipStream_t hs = (hipStream_t)stream;
+  st = finish(launch_fwd<true>(p, d, causal != 0, pad, grid, (int)chunks, hs));
+  if (st != ATTN_OK) return st;
+  const int64_t rows = BH * s_q;
+  const int mgrid = (int)((rows + 3) / 4);
+  if (d == 128)
+    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(mgrid), dim3(256), 0, hs, p.o_part, p.lse_part,
+                       (uint16_t*)out, lse, rows, (int)chunks);
+  else
+    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(mgrid), dim3(256), 0, hs, p.o_part, p.lse_part,
+                       (uint16_t*)out, lse, rows, (int)chunks);
+  return finish(hipGetLastError());
 }
 
 extern "C" const char* attn_status_str(int status) {
@@ -681,6 +844,7 @@ extern "C" const char* attn_status_str(int status) {
     case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS: out or lse overlaps another buffer";
     case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE: scale is NaN or infinite";
     case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: the HIP runtime refused the launch";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: the workspace is smaller than required";
     default: return "unknown attn status";
   }
 }

@@ -37,7 +37,8 @@ typedef enum attn_status {
   ATTN_ERR_ALIGN = 4,    /* q, k, v, out not 16-byte aligned, or lse not 4-byte     */
   ATTN_ERR_ALIAS = 5,    /* out or lse overlaps an input, or out overlaps lse       */
   ATTN_ERR_SCALE = 6,    /* scale is NaN or infinite                                */
-  ATTN_ERR_LAUNCH = 7    /* the HIP runtime refused the kernel launch               */
+  ATTN_ERR_LAUNCH = 7,   /* the HIP runtime refused the kernel launch               */
+  ATTN_ERR_WORKSPACE = 8 /* attn_fwd_split: workspace smaller than required         */
 } attn_status;
 
 /*
@@ -87,6 +88,52 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 int attn_fwd_validate(const void* q, const void* k, const void* v, const void* out,
                       const float* lse, int64_t B, int64_t H, int64_t s_q, int64_t s_k,
                       int64_t d, float scale, int causal, const uint8_t* key_padding_mask);
+
+/*
+ * attn_fwd_split - the same result as attn_fwd, computed over n_splits
+ * contiguous chunks of the keys (each a multiple of 64 keys; at most one chunk
+ * per 64 keys is used) that run as independent workgroups, followed by a merge
+ * of the chunks' partial results.
+ *
+ * Why: the news.hamidun.com glossary entry "Flash attention" (fourth
+ * paragraph) names inference frameworks and Ring Attention, which partitions
+ * the method's work over keys; with few query rows per (b, h) the plain launch
+ * has fewer workgroups than the device has compute units, and splitting the
+ * keys fills it. The merge follows from the softmax definition (onecalc.app
+ * "Attention memory", section "What this memory is"): for chunk results O_z
+ * with log-sum-exps lse_z, lse = ln sum_z exp(lse_z) and
+ * O = sum_z exp(lse_z - lse) O_z.
+ *
+ * Arguments: as attn_fwd, plus
+ *   n_splits         requested number of key chunks, 1 .. 65535 (1, or a
+ *                    problem with a single 64-key tile, runs attn_fwd and
+ *                    needs no workspace)
+ *   workspace        caller-owned device memory, 256-byte aligned, of at least
+ *                    attn_fwd_split_workspace_bytes(B, H, s_q, d, chunks)
+ *                    bytes, chunks = min(n_splits, ceil(s_k / 64)); it holds
+ *                    the float32 partial outputs [chunk][B*H][s_q][d] and
+ *                    log-sum-exps [chunk][B*H][s_q]; its contents on entry are
+ *                    ignored and on return are unspecified
+ *   workspace_bytes  its size in bytes
+ *
+ * The library allocates nothing; two kernels are enqueued on `stream`, and
+ * concurrent calls must not share a workspace. Additional statuses:
+ * ATTN_ERR_SHAPE for n_splits out of range, ATTN_ERR_NULL for a missing
+ * workspace, ATTN_ERR_ALIGN for a misaligned one, ATTN_ERR_WORKSPACE when it
+ * is too small, ATTN_ERR_ALIAS when it overlaps a tensor argument.
+ */
+int attn_fwd_split(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d,
+                   float scale, int causal, const uint8_t* key_padding_mask,
+                   int64_t n_splits, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_split_workspace_bytes - workspace bytes attn_fwd_split needs for
+ * `n_splits` chunks (0 when n_splits == 1); -1 for invalid sizes (negative
+ * sizes, d not 64 or 128, n_splits outside 1 .. 65535). Host-only.
+ */
+int64_t attn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t s_q, int64_t d,
+                                       int64_t n_splits);
 
 /* attn_status_str - a static, human-readable name for a status code. */
 const char* attn_status_str(int status);

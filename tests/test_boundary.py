@@ -34,7 +34,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert names == ["attn_fwd", "attn_fwd_validate", "attn_last_hip_error", "attn_status_str"]
+    assert names == ["attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_bytes",
+                     "attn_fwd_validate", "attn_last_hip_error", "attn_status_str"]
     for n in names:
         assert hasattr(lib, n), n
     dyn = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
@@ -141,3 +142,62 @@ def test_fwd_rejects_cpu_tensors(lib):
         E.fwd(q, q, q)
     with pytest.raises(TypeError):
         E.fwd(q.float(), q, q)
+
+
+# ---------------------------------------------------------------- key-split entry point
+WS = 7 << 40  # fake, 256-byte aligned workspace address, overlapping nothing
+
+
+def ws_bytes(B, H, s_q, d, n):
+    if n == 1:
+        return 0
+    rows = B * H * s_q
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    return up(n * rows * d * 4) + up(n * rows * 4)
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 100, 128, 1), (2, 3, 100, 128, 2), (1, 32, 1024, 128, 4),
+                                   (4, 16, 2048, 64, 3), (1, 1, 1, 64, 65535)])
+def test_split_workspace_bytes(lib, shape):
+    assert E.attn_fwd_split_workspace_bytes(*shape) == ws_bytes(*shape)
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 100, 96, 2), (2, 3, 100, 128, 0), (2, 3, 100, 128, 65536),
+                                   (-1, 3, 100, 128, 2)])
+def test_split_workspace_bytes_rejects(lib, shape):
+    assert E.attn_fwd_split_workspace_bytes(*shape) == -1
+
+
+def call_split(n_splits=4, workspace=WS, workspace_bytes=None, **over):
+    a = dict(GOOD, **over)
+    chunks = min(n_splits, (a["s_k"] + 63) // 64) if n_splits >= 1 else n_splits
+    if workspace_bytes is None:
+        workspace_bytes = ws_bytes(a["B"], a["H"], a["s_q"], a["d"], max(chunks, 1))
+    args = [a[n] for n in ("q", "k", "v", "out", "lse", "B", "H", "s_q", "s_k", "d", "scale",
+                           "causal", "key_padding_mask")]
+    return E.attn_fwd_split(*args, n_splits, workspace, workspace_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_splits=0), E.ATTN_ERR_SHAPE),
+    (dict(n_splits=-3), E.ATTN_ERR_SHAPE),
+    (dict(n_splits=65536), E.ATTN_ERR_SHAPE),
+    (dict(workspace=None), E.ATTN_ERR_NULL),
+    (dict(workspace=WS + 16), E.ATTN_ERR_ALIGN),
+    (dict(workspace_bytes=1000), E.ATTN_ERR_WORKSPACE),
+    (dict(workspace=OUT - 256), E.ATTN_ERR_ALIAS),
+    (dict(workspace=KPM), E.ATTN_ERR_ALIAS),
+    (dict(q=None), E.ATTN_ERR_NULL),
+    (dict(d=96), E.ATTN_ERR_HEAD_DIM),
+    (dict(scale=float("nan")), E.ATTN_ERR_SCALE),
+])
+def test_split_rejected_before_launch(lib, kw, code):
+    over = {k: v for k, v in kw.items() if k in GOOD}
+    rest = {k: v for k, v in kw.items() if k not in GOOD}
+    assert call_split(**rest, **over) == code
+
+
+def test_split_empty_problems_are_no_ops(lib):
+    null = dict(q=None, k=None, v=None, out=None, lse=None)
+    assert call_split(B=0, **null) == E.ATTN_OK
+    assert call_split(s_q=0, **null) == E.ATTN_OK

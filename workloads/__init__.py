@@ -24,6 +24,7 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "HEADLINE",
+    "SPLIT_WORKLOADS",
     "round_to_bf16",
     "bf16_bits_to_f32",
     "generate",
@@ -96,6 +97,15 @@ WORKLOADS = (
 
 # The configuration the headline throughput is quoted on (s = 8192, d = 128, causal).
 HEADLINE = WORKLOADS[2]
+
+# Shapes for the key-split forward: a 1024-query chunk against the glossary
+# example's 32,000-token context (32768 keys), the prefill step of an inference
+# framework (the glossary's fourth paragraph). A plain launch has only
+# ceil(1024 / 256) * 32 = 128 workgroups here, half the device's compute units.
+SPLIT_WORKLOADS = (
+    Workload("B=1,H=32,s_q=1024,s_k=32768,d=128,prefill-chunk", 1, 32, 1024, 32768, 128, False,
+             False, 1.0, 44006),
+)
 
 
 def padding_mask_from_lengths(lengths: np.ndarray, s_k: int) -> np.ndarray:
