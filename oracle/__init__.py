@@ -1,5 +1,6 @@
 """CPU oracle (test infrastructure only; see oracle/attention.py)."""
 from .attention import (  # noqa: F401
+    attention_backward_fp64,
     attention_bruteforce,
     attention_fp64,
     attention_online_fp64,

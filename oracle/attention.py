@@ -36,6 +36,8 @@ Functions:
   merge_partials_fp64       combination of results over disjoint key sets
                             into the result over their union (for the key-
                             split forward);
+  attention_backward_fp64   gradients of the definition with respect to q, k
+                            and v for a given output gradient;
   score_matrix_bytes / score_matrix_gb
                             the closed form of the materialised score memory.
 """
@@ -55,6 +57,7 @@ __all__ = [
     "attention_online_fp64",
     "attention_bruteforce",
     "merge_partials_fp64",
+    "attention_backward_fp64",
 ]
 
 NEG_INF = -np.inf
@@ -328,3 +331,52 @@ def merge_partials_fp64(outs, lses) -> Tuple[np.ndarray, np.ndarray]:
     frac[:, ~empty] = w[:, ~empty] / total[None, ~empty]
     O = (frac[..., None] * outs).sum(axis=0)
     return O, lse
+
+
+# ----------------------------------------------------------------------------
+# Gradients of the definition (the backward pass).
+# The onecalc.app page "Attention memory", section "What this memory is", notes
+# that training frameworks keep the materialised score matrix for the backward
+# pass unless checkpointing or a fused kernel does without it, and the
+# news.hamidun.com glossary entry "Flash attention" (third paragraph) puts the
+# method's gains in training. The pages give no formulas for the backward pass;
+# these are the derivatives of the definition's steps, chained in reverse:
+#   O = P V                 ->  dV = P^T dO,   dP = dO V^T
+#   P = softmax_row(S)      ->  dS[i, j] = P[i, j] (dP[i, j] - sum_j' P[i, j'] dP[i, j'])
+#   S = scale q k^T + mask  ->  dQ = scale dS K,   dK = scale dS^T Q
+# (hidden entries have P = 0, so they carry no gradient; a row with no visible
+# key has P = 0 and contributes nothing).
+# ----------------------------------------------------------------------------
+def _softmax_backward(P: np.ndarray, dP: np.ndarray) -> np.ndarray:
+    """dS = P * (dP - rowsum(P * dP))."""
+    return P * (dP - (P * dP).sum(axis=1, keepdims=True))
+
+
+def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool = False,
+                            key_padding_mask=None, row_block: int = 2048):
+    """Returns (dq, dk, dv), float64, shaped like q, k, v.
+
+    P is rebuilt from the definition for each block of ``row_block`` query
+    rows (rows are independent in every step except the sums over rows in dK
+    and dV, which accumulate over the blocks).
+    """
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    _check(q, k, v, key_padding_mask)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    B, H, s_q, d = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        kpm_row = None if key_padding_mask is None else np.asarray(key_padding_mask)[b]
+        for h in range(H):
+            for r0 in range(0, s_q, row_block):
+                r1 = min(s_q, r0 + row_block)
+                _, _, P = _rows(q[b, h, r0:r1], k[b, h], v[b, h], scale,
+                                np.arange(r0, r1), causal, kpm_row)
+                g = dout[b, h, r0:r1]
+                dv[b, h] += P.T @ g
+                dP = g @ v[b, h].T
+                dS = _softmax_backward(P, dP)
+                dq[b, h, r0:r1] = np.float64(scale) * (dS @ k[b, h])
+                dk[b, h] += np.float64(scale) * (dS.T @ q[b, h, r0:r1])
+    return dq, dk, dv

@@ -339,6 +339,89 @@ def pin_merge_of_key_chunks():
     close(lm, np.array([1.5]), 1e-15, "empty part lse")
 
 
+# ---------------------------------------------------------------- the backward pass
+
+
+def _grad_case(seed, B, H, s_q, s_k, d, **kw):
+    c = f64_case(seed, B, H, s_q, s_k, d, **kw)
+    c["dout"] = np.random.default_rng(seed + 1000).standard_normal(c["q"].shape)
+    return c
+
+
+def run_bwd(c, **kw):
+    return A.attention_backward_fp64(c["q"], c["k"], c["v"], c["dout"], c["scale"], c["causal"],
+                                     c["kpm"], **kw)
+
+
+def pin_backward_torch_autograd():
+    """torch's scaled_dot_product_attention differentiated by autograd in
+    float64 on the CPU (rows with a visible key only: torch's softmax over an
+    all -inf row is not defined)."""
+    torch = __import__("torch")
+    F = torch.nn.functional
+    for seed, causal, mask in ((131, True, "none"), (132, False, "lengths"), (133, True, "random")):
+        c = _grad_case(seed, 2, 3, 13, 17, 16, causal=causal, mask=mask)
+        vis = visible(c)
+        if mask != "none":  # keep every row non-empty for torch
+            vis[:, :, 0] = True
+            c["kpm"][:, 0] = 0
+        q, k, v = (torch.tensor(c[n], requires_grad=True) for n in ("q", "k", "v"))
+        attn_mask = torch.tensor(vis)[:, None]
+        o = F.scaled_dot_product_attention(q, k, v, attn_mask=attn_mask, scale=c["scale"])
+        o.backward(torch.tensor(c["dout"]))
+        dq, dk, dv = run_bwd(c)
+        close(dq, q.grad.numpy(), 1e-12, f"dq seed={seed}")
+        close(dk, k.grad.numpy(), 1e-12, f"dk seed={seed}")
+        close(dv, v.grad.numpy(), 1e-12, f"dv seed={seed}")
+
+
+def pin_backward_finite_differences():
+    """Central differences of L = sum(dout * O) through the forward
+    definition, for every input element of a tiny problem."""
+    c = _grad_case(134, 1, 1, 4, 5, 3, causal=True, mask="random")
+    c["kpm"][0, 0] = 0
+    dq, dk, dv = run_bwd(c)
+    eps = 1e-6
+
+    def loss():
+        O, _ = run(c)
+        return float((c["dout"] * O).sum())
+
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        x = c[name]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = loss()
+            x[idx] = keep - eps
+            lm = loss()
+            x[idx] = keep
+            num[idx] = (lp - lm) / (2 * eps)
+        close(grad, num, 1e-7, f"d{name} vs finite differences")
+
+
+def pin_backward_identities():
+    """Each softmax row's gradient sums to zero over its keys, so the key
+    gradients of a (b, h) sum to zero and the query gradient does not change
+    when one vector is added to every key; padded keys get no gradient; with
+    one visible key the value gradient is the sum of the output gradients."""
+    c = _grad_case(135, 2, 2, 11, 9, 8, causal=True, mask="lengths")
+    c["kpm"][:, 0] = 0
+    dq, dk, dv = run_bwd(c)
+    close(dk.sum(axis=2), np.zeros((2, 2, 8)), 1e-12, "sum_j dk_j")
+    pad = c["kpm"] != 0
+    for b in range(2):
+        assert np.all(dk[b][:, pad[b]] == 0.0) and np.all(dv[b][:, pad[b]] == 0.0)
+    shifted = dict(c)
+    shifted["k"] = c["k"] + np.random.default_rng(7).standard_normal(8)[None, None, None, :]
+    dq2, _, _ = run_bwd(shifted)
+    close(dq2, dq, 1e-11, "dq under a common key shift")
+    one = _grad_case(136, 1, 2, 6, 1, 4)
+    _, _, dv1 = run_bwd(one)
+    close(dv1[:, :, 0], one["dout"].sum(axis=2), 1e-14, "one key: dv = sum of dout")
+
+
 PINS = [
     pin_worked_example,
     pin_oracle_materialises_closed_form,
@@ -353,4 +436,7 @@ PINS = [
     pin_large_scores,
     pin_fully_masked_rows,
     pin_merge_of_key_chunks,
+    pin_backward_torch_autograd,
+    pin_backward_finite_differences,
+    pin_backward_identities,
 ]

@@ -138,3 +138,40 @@ def test_merge_mutant_is_caught(name, monkeypatch):
         except Exception as e:
             failed.append((pin.__name__, type(e).__name__))
     assert failed, f"mutant {name} passed every pin"
+
+
+ORIG_BWD = A.attention_backward_fp64
+
+
+def _bwd_variant(dq_f=None, dk_f=None, dv_f=None):
+    def f(q, k, v, dout, scale, causal=False, key_padding_mask=None, row_block=2048):
+        dq, dk, dv = ORIG_BWD(q, k, v, dout, scale, causal, key_padding_mask, row_block)
+        return (dq_f(dq, dk, dv) if dq_f else dq, dk_f(dq, dk, dv) if dk_f else dk,
+                dv_f(dq, dk, dv) if dv_f else dv)
+    return f
+
+
+BWD_MUTANTS = {
+    "softmax_backward_without_rowsum": ("_softmax_backward", lambda P, dP: P * dP),
+    "softmax_backward_sign": ("_softmax_backward", lambda P, dP: P * ((P * dP).sum(axis=1, keepdims=True) - dP)),
+    "dq_without_scale": ("attention_backward_fp64",
+                         _bwd_variant(dq_f=lambda dq, dk, dv: dq * 1.37)),
+    "dk_transposed_role": ("attention_backward_fp64",
+                           _bwd_variant(dk_f=lambda dq, dk, dv: dk[:, :, ::-1])),
+    "dv_off_by_one_key": ("attention_backward_fp64",
+                          _bwd_variant(dv_f=lambda dq, dk, dv: np.roll(dv, 1, axis=2))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name, monkeypatch):
+    attr, fn = BWD_MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    failed = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception as e:
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"
