@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--split-workload", type=int, default=None,
                     help="index into workloads.SPLIT_WORKLOADS: time the key-split entry point "
                          "(attn_fwd_split) on that shape instead")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (attn_bwd) of the workload instead; FLOPs "
+                         "counted as 2.5x the forward's (five products of its size, one of "
+                         "them the recomputed scores)")
     ap.add_argument("--splits", type=int, default=4,
                     help="key chunks for --split-workload (1 = the plain launch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -76,11 +80,12 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, g, target_s):
-    """Time the oracle on whole heads of the same workload until ~target_s."""
+def cpu_baseline(w, g, target_s, backward=False):
+    """Time the oracle on whole heads of the same workload until ~target_s
+    (its gradients, with a seeded output gradient, for the backward pass)."""
     import numpy as np
 
-    from oracle import attention_fp64
+    from oracle import attention_backward_fp64, attention_fp64
     from workloads import bf16_bits_to_f32
 
     threads = os.cpu_count()
@@ -91,14 +96,20 @@ def cpu_baseline(w, g, target_s):
             threads = blas[0]
     except Exception:
         pass
-    per_head = w.flops() / (w.B * w.H)
+    per_head = w.flops() / (w.B * w.H) * (2.5 if backward else 1.0)
     heads, spent = 0, 0.0
+    rng = np.random.default_rng(w.seed + 2)
     for b in range(w.B):
         for h in range(w.H):
             q, k, v = (bf16_bits_to_f32(g[n][b:b + 1, h:h + 1]) for n in ("q", "k", "v"))
             kpm = None if g["kpm"] is None else g["kpm"][b:b + 1]
-            t0 = time.perf_counter()
-            attention_fp64(q, k, v, float(g["scale"]), w.causal, kpm)
+            if backward:
+                dout = rng.standard_normal(q.shape)
+                t0 = time.perf_counter()
+                attention_backward_fp64(q, k, v, dout, float(g["scale"]), w.causal, kpm)
+            else:
+                t0 = time.perf_counter()
+                attention_fp64(q, k, v, float(g["scale"]), w.causal, kpm)
             spent += time.perf_counter() - t0
             heads += 1
             if spent >= target_s:
@@ -110,7 +121,7 @@ def cpu_baseline(w, g, target_s):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"float64 NumPy oracle (materialises each head's s x s scores, row blocks "
+        "sample": (f"float64 NumPy oracle{' gradients' if backward else ''} (materialises each head's s x s scores, row blocks "
                    f"of 2048) on {heads} of {w.B * w.H} heads of {w.name}: {spent:.1f} s on "
                    f"{threads} BLAS threads, {platform.processor() or platform.machine()}; "
                    f"FLOPs counted with the metric formula"),
@@ -147,7 +158,25 @@ def main():
     args = (q, k, v, out, lse, w.B, w.H, w.s_q, w.s_k, w.d, float(g["scale"]), w.causal, kpm,
             stream.cuda_stream)
 
-    if split:
+    if a.backward:
+        # forward outputs and a seeded output gradient, before any timing
+        st = E.attn_fwd(*args)
+        if st != E.ATTN_OK:
+            raise E.AttnError(st)
+        from workloads import round_to_bf16
+        gnp = round_to_bf16(np.random.default_rng(w.seed + 1).standard_normal(
+            (w.B, w.H, w.s_q, w.d), dtype=np.float32))
+        dout = torch.from_numpy(gnp.view(np.int16)).view(torch.bfloat16).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws_bytes = E.attn_bwd_workspace_bytes(w.B, w.H, w.s_q)
+        bws = torch.empty(max(bws_bytes, 256), dtype=torch.uint8, device=dev)
+
+        def step():
+            st = E.attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, w.B, w.H, w.s_q, w.s_k, w.d,
+                            float(g["scale"]), w.causal, kpm, bws, bws.numel(), stream.cuda_stream)
+            if st != E.ATTN_OK:
+                raise E.AttnError(st)
+    elif split:
         chunks = max(1, min(a.splits, (w.s_k + 63) // 64))
         ws_bytes = E.attn_fwd_split_workspace_bytes(w.B, w.H, w.s_q, w.d, chunks)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # outside the timed region
@@ -192,11 +221,15 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    flops = w.flops()
-    algorithmic_bytes = 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d + 2 * w.B * w.H * w.s_q * w.d \
-        + 4 * w.B * w.H * w.s_q
+    flops = w.flops() * (2.5 if a.backward else 1.0)
+    if a.backward:  # read q, out, dout, k, v, lse; write dq, dk, dv
+        algorithmic_bytes = 2 * w.B * w.H * (3 * w.s_q + 2 * w.s_k) * w.d + 4 * w.B * w.H * w.s_q \
+            + 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d
+    else:
+        algorithmic_bytes = 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d + 2 * w.B * w.H * w.s_q * w.d \
+            + 4 * w.B * w.H * w.s_q
     traffic, traffic_detail = None, {"algorithmic_bytes": algorithmic_bytes}
-    measured = MEASURED_TRAFFIC.get(w.name)
+    measured = None if (a.backward or split) else MEASURED_TRAFFIC.get(w.name)
     if measured is not None:
         import hashlib
         with open(KERNEL_SOURCE, "rb") as f:
@@ -235,12 +268,16 @@ def main():
             "traffic": traffic,
             "traffic_unit": "bytes per launch",
             "traffic_detail": traffic_detail,
-            "kernel": ("attn_fwd_kernel (key-split) + attn_merge_kernel" if split
+            "kernel": ("attn_bwd_dq_kernel + attn_bwd_dkv_kernel" if a.backward
+                       else "attn_fwd_kernel (key-split) + attn_merge_kernel" if split
                        else "attn_fwd_kernel"),
             "kernel_avg_ms": round(kern_avg_ms, 5),
             "kernel_min_ms": round(min(kern_ms), 5),
         },
     }
+    if a.backward:
+        res["config"]["pass"] = "backward"
+        res["metric"] = METRIC + " (backward pass: dq, dk, dv)"
     if split:
         res["config"]["n_splits"] = a.splits
         res["config"]["entry_point"] = "attn_fwd_split"
@@ -250,7 +287,7 @@ def main():
         useful = sum(4.0 * w.H * w.s_q * int(n) * w.d for n in lengths)
         res["useful_tflops"] = round(useful * a.steps / wall / 1e12, 2)
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, g, a.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, g, a.cpu_seconds, backward=a.backward)
     print(json.dumps(res), flush=True)
 
 

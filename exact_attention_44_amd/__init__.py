@@ -17,8 +17,8 @@ __all__ = [
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
     "ATTN_ERR_ALIAS", "ATTN_ERR_SCALE", "ATTN_ERR_LAUNCH", "ATTN_ERR_WORKSPACE", "AttnError",
     "load_library", "attn_fwd", "attn_fwd_validate", "attn_fwd_split",
-    "attn_fwd_split_workspace_bytes", "attn_status_str", "attn_last_hip_error", "fwd",
-    "fwd_split", "LIB_PATH",
+    "attn_fwd_split_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
+    "attn_last_hip_error", "fwd", "fwd_split", "bwd", "LIB_PATH",
 ]
 
 ATTN_OK = 0
@@ -71,6 +71,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_split.restype = ctypes.c_int
     lib.attn_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
     lib.attn_fwd_split_workspace_bytes.restype = i64
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                             ctypes.c_float, ctypes.c_int, vp, vp, i64, vp]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.attn_bwd_workspace_bytes.restype = i64
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -116,6 +121,20 @@ def attn_fwd_split(q, k, v, out, lse, B: int, H: int, s_q: int, s_k: int, d: int
 
 def attn_fwd_split_workspace_bytes(B: int, H: int, s_q: int, d: int, n_splits: int) -> int:
     return load_library().attn_fwd_split_workspace_bytes(B, H, s_q, d, n_splits)
+
+
+def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B: int, H: int, s_q: int, s_k: int, d: int,
+             scale: float, causal: bool, key_padding_mask, workspace, workspace_bytes: int,
+             stream) -> int:
+    """The C entry point attn_bwd with the same arguments."""
+    return load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, s_q, s_k, d, float(scale),
+                                   1 if causal else 0, _ptr(key_padding_mask), _ptr(workspace),
+                                   workspace_bytes, stream)
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, s_q: int) -> int:
+    return load_library().attn_bwd_workspace_bytes(B, H, s_q)
 
 
 def attn_status_str(status: int) -> str:
@@ -200,3 +219,38 @@ def fwd_split(q, k, v, *, n_splits: int, causal: bool = False, key_padding_mask=
     if st != ATTN_OK:
         raise AttnError(st)
     return out, lse
+
+
+def bwd(q, k, v, out, dout, lse, *, causal: bool = False, key_padding_mask=None,
+        scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of fwd's output for the output gradient `dout`
+    (attn_bwd); `out` and `lse` are what fwd returned for q, k, v. All bf16
+    tensors contiguous on one device; a workspace of
+    attn_bwd_workspace_bytes(B, H, s_q) bytes is allocated with torch when
+    not given."""
+    import torch
+
+    B, H, s_q, s_k, d = _check_inputs(q, k, v, key_padding_mask)
+    for name, t in (("out", out), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or tuple(t.shape) != (B, H, s_q, d):
+            raise ValueError(f"{name} must be bfloat16 {(B, H, s_q, d)}")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, s_q) or not lse.is_cuda:
+        raise ValueError(f"lse must be float32 {(B, H, s_q)} on the device")
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(q.device):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        need = attn_bwd_workspace_bytes(B, H, s_q)
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, H, s_q, s_k, d, scale, causal,
+                      key_padding_mask, workspace, ws_bytes, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return dq, dk, dv

@@ -40,19 +40,11 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "attn_common.h"
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+using namespace attn_detail;
 
 struct FwdParams {
   const uint16_t* q;
@@ -70,46 +62,6 @@ struct FwdParams {
   uint32_t q_xor;   // 0x80008000 when scale < 0: Q negated, so c stays > 0
   uint32_t q_and;   // 0 when scale == 0: Q zeroed, scores are exactly 0
 };
-
-// Key row fed to accumulator row m of the score MFMA (see file comment).
-__device__ __forceinline__ int key_of_row(int m) {
-  const int a = m >> 3, hh = (m >> 2) & 1, b = m & 3;
-  return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + b;
-}
-
-__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  f32x2_t f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-// Buffer resource over [base, base + bytes): loads past the end return zero,
-// which pads ragged query and key tails without branches.
-// The fields are wave-uniform by construction; readfirstlane states that to
-// the compiler so the descriptor stays in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  void* ub = (void*)(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)n, 0x00020000);
-}
-
-// 16 bytes per lane from the buffer straight into LDS: lane i's bytes land at
-// dst + 16 i (dst is wave-uniform). A device function of its own, so the host
-// compilation pass never sees the LDS address-space cast.
-__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t byte_off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, byte_off, 0,
-                                          0, 0);
-}
-
-__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
-}
 
 template <int D, bool CAUSAL, bool PADMASK, bool SPLIT>
 __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
@@ -587,7 +539,6 @@ constexpr int rows_per_block() {
   return 256;
 }
 
-thread_local int g_last_hip_error = 0;
 
 template <int D, bool CAUSAL, bool PADMASK, bool SPLIT>
 hipError_t launch(const FwdParams& p, int grid, int chunks, hipStream_t stream) {

@@ -135,6 +135,54 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* out, float
 int64_t attn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t s_q, int64_t d,
                                        int64_t n_splits);
 
+/*
+ * attn_bwd - enqueue the backward pass of attn_fwd on `stream`: the gradients
+ * of O with respect to q, k and v for a given gradient dO of the output.
+ *
+ * The onecalc.app page "Attention memory" (section "What this memory is")
+ * notes that training frameworks keep the materialised score matrix for the
+ * backward pass unless a fused kernel does without it; this one does: the
+ * weights are rebuilt tile by tile from the forward pass's log-sum-exp,
+ * P = exp(scale q.k - lse), and nothing of size s_q x s_k is stored. The
+ * gradients are the chain rule through the definition (the pages give no
+ * formulas): dV = P^T dO, dP = dO V^T, D_i = dO_i . O_i,
+ * dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ *
+ * Arguments (caller-owned DEVICE memory, dense row-major):
+ *   q, k, v, causal, key_padding_mask, scale, B, H, s_q, s_k, d
+ *                     as given to attn_fwd
+ *   out    bf16 [B, H, s_q, d]  attn_fwd's output for these inputs
+ *   dout   bf16 [B, H, s_q, d]  gradient of the loss with respect to out
+ *   lse    f32  [B, H, s_q]     attn_fwd's log-sum-exp for these inputs
+ *                               (-inf marks a row with no visible key)
+ *   dq     bf16 [B, H, s_q, d]  written
+ *   dk, dv bf16 [B, H, s_k, d]  written (zero for keys no query sees)
+ *   workspace        caller-owned device memory, 256-byte aligned, of at
+ *                    least attn_bwd_workspace_bytes(B, H, s_q) bytes (it
+ *                    holds D, float32 [B, H, s_q]); contents on entry are
+ *                    ignored and on return unspecified
+ *   workspace_bytes  its size
+ *   stream           a hipStream_t (NULL = the default stream)
+ *
+ * Two kernels run in order on `stream` (dq and D, then dk and dv); the library
+ * allocates nothing, and concurrent calls must not share a workspace.
+ * Returns ATTN_OK or: ATTN_ERR_NULL (a required pointer is NULL),
+ * ATTN_ERR_SHAPE, ATTN_ERR_HEAD_DIM, ATTN_ERR_SCALE (as attn_fwd),
+ * ATTN_ERR_ALIGN (a bf16 tensor not 16-byte aligned, lse not 4-byte, the
+ * workspace not 256-byte), ATTN_ERR_WORKSPACE (workspace too small),
+ * ATTN_ERR_ALIAS (an output overlaps an input or another output),
+ * ATTN_ERR_LAUNCH.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv,
+             int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d,
+             float scale, int causal, const uint8_t* key_padding_mask,
+             void* workspace, int64_t workspace_bytes, void* stream);
+
+/* attn_bwd_workspace_bytes - workspace bytes attn_bwd needs (-1 for negative
+ * sizes). Host-only. */
+int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t s_q);
+
 /* attn_status_str - a static, human-readable name for a status code. */
 const char* attn_status_str(int status);
 

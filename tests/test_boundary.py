@@ -34,8 +34,9 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert names == ["attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_bytes",
-                     "attn_fwd_validate", "attn_last_hip_error", "attn_status_str"]
+    assert names == ["attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_split",
+                     "attn_fwd_split_workspace_bytes", "attn_fwd_validate", "attn_last_hip_error",
+                     "attn_status_str"]
     for n in names:
         assert hasattr(lib, n), n
     dyn = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
@@ -201,3 +202,52 @@ def test_split_empty_problems_are_no_ops(lib):
     null = dict(q=None, k=None, v=None, out=None, lse=None)
     assert call_split(B=0, **null) == E.ATTN_OK
     assert call_split(s_q=0, **null) == E.ATTN_OK
+
+
+# ---------------------------------------------------------------- backward entry point
+DO, DQ, DK, DV, BWS = (8 << 40), (9 << 40), (10 << 40), (11 << 40), (12 << 40)
+BGOOD = dict(q=Q, k=K, v=V, out=OUT, dout=DO, lse=LSE, dq=DQ, dk=DK, dv=DV, B=2, H=3, s_q=100,
+             s_k=90, d=128, scale=0.1, causal=1, key_padding_mask=KPM, workspace=BWS,
+             workspace_bytes=2 * 3 * 100 * 4 + 256)
+
+
+def call_bwd(**over):
+    a = dict(BGOOD, **over)
+    names = ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "B", "H", "s_q", "s_k", "d",
+             "scale", "causal", "key_padding_mask", "workspace", "workspace_bytes")
+    return E.attn_bwd(*[a[n] for n in names], None)
+
+
+def test_bwd_workspace_bytes(lib):
+    assert E.attn_bwd_workspace_bytes(2, 3, 100) == 2560
+    assert E.attn_bwd_workspace_bytes(1, 32, 8192) == 32 * 8192 * 4
+    assert E.attn_bwd_workspace_bytes(-1, 3, 100) == -1
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dout=None), E.ATTN_ERR_NULL),
+    (dict(dq=None), E.ATTN_ERR_NULL),
+    (dict(dk=None), E.ATTN_ERR_NULL),
+    (dict(lse=None), E.ATTN_ERR_NULL),
+    (dict(workspace=None), E.ATTN_ERR_NULL),
+    (dict(d=96), E.ATTN_ERR_HEAD_DIM),
+    (dict(s_q=-1), E.ATTN_ERR_SHAPE),
+    (dict(scale=float("inf")), E.ATTN_ERR_SCALE),
+    (dict(dq=DQ + 8), E.ATTN_ERR_ALIGN),
+    (dict(lse=LSE + 2), E.ATTN_ERR_ALIGN),
+    (dict(workspace=BWS + 64), E.ATTN_ERR_ALIGN),
+    (dict(workspace_bytes=100), E.ATTN_ERR_WORKSPACE),
+    (dict(dq=Q + 256), E.ATTN_ERR_ALIAS),
+    (dict(dv=DK + 512), E.ATTN_ERR_ALIAS),
+    (dict(dk=KPM - 16), E.ATTN_ERR_ALIAS),
+    (dict(workspace=DQ), E.ATTN_ERR_ALIAS),
+])
+def test_bwd_rejected_before_launch(lib, over, code):
+    assert call_bwd(**over) == code
+
+
+def test_bwd_empty_problems_are_no_ops(lib):
+    null = dict(q=None, k=None, v=None, out=None, dout=None, lse=None, dq=None, dk=None, dv=None,
+                workspace=None)
+    assert call_bwd(B=0, **null) == E.ATTN_OK
+    assert call_bwd(s_q=0, s_k=0, **null) == E.ATTN_OK
