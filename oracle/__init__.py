@@ -10,3 +10,4 @@ from .attention import (  # noqa: F401
     score_matrix_bytes,
     score_matrix_gb,
 )
+from .fp8 import attention_fp8_fp64, dequantize_heads, e4m3_to_fp64  # noqa: F401

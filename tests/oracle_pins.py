@@ -13,7 +13,10 @@ What the pins stand on:
     section), implemented separately in the oracle, which must reach the same
     result (the glossary entry "Flash attention" states the results agree);
   * pure-Python brute force and a high-precision Decimal evaluation;
-  * torch's CPU scaled_dot_product_attention and logsumexp in float64.
+  * torch's CPU scaled_dot_product_attention and logsumexp in float64;
+  * for the 8-bit-float inputs: torch's float8_e4m3fn dtype and the field
+    layout of the OCP E4M3 format (closed-form code values), plus the scaling
+    identities of per-head descale factors.
 """
 from __future__ import annotations
 
@@ -26,7 +29,8 @@ import numpy as np
 import torch
 
 import oracle.attention as A
-from workloads import WORKLOADS, bf16_bits_to_f32, generate, random_case
+import oracle.fp8 as F8
+from workloads import WORKLOADS, bf16_bits_to_f32, generate, quantize_heads_e4m3, random_case
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -422,6 +426,90 @@ def pin_backward_identities():
     close(dv1[:, :, 0], one["dout"].sum(axis=2), 1e-14, "one key: dv = sum of dout")
 
 
+def pin_e4m3_decode_against_torch():
+    """Every one of the 256 E4M3 codes decodes to the value torch's float8_e4m3fn
+    dtype (the OCP E4M3 format) widens to, sign of zero and NaN codes included."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = F8.e4m3_to_fp64(codes)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(got), nan), "NaN codes differ"
+    assert np.array_equal(got[~nan], ref[~nan]), "decoded values differ from torch"
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])), "signs differ"
+
+
+def pin_e4m3_decode_closed_forms():
+    """Code values that follow from the field layout (bias 7, 3 mantissa bits,
+    subnormal step 2^-9, largest finite 448), monotonicity and sign symmetry."""
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x04: 0.5 * 2.0 ** -6, 0x07: 7 * 2.0 ** -9,
+             0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6, 0x30: 0.5, 0x38: 1.0, 0x39: 1.125,
+             0x3F: 1.875, 0x40: 2.0, 0x55: 1.625 * 2.0 ** 3, 0x77: 1.875 * 2.0 ** 7,
+             0x78: 256.0, 0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, want in table.items():
+        got = float(F8.e4m3_to_fp64(np.array([c], np.uint8))[0])
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (hex(c), got, want)
+    assert np.isnan(F8.e4m3_to_fp64(np.array([0x7F, 0xFF], np.uint8))).all()
+    pos = F8.e4m3_to_fp64(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0), "positive codes must increase"
+    neg = F8.e4m3_to_fp64(np.arange(0x80, 0xFF, dtype=np.uint8))
+    assert np.array_equal(neg, -pos), "negative codes mirror positive ones"
+
+
+def _fp8_case(seed, B, H, s_q, s_k, d, **kw):
+    c = random_case(seed, B, H, s_q, s_k, d, **kw)
+    out = dict(causal=c["causal"], kpm=c["kpm"], scale=float(c["scale"]))
+    for n in ("q", "k", "v"):
+        x = bf16_bits_to_f32(c[n])
+        bits, ds = quantize_heads_e4m3(x)
+        out[n + "8"], out["d" + n] = bits, ds
+    return out
+
+
+def run_fp8(c, **kw):
+    return F8.attention_fp8_fp64(c["q8"], c["k8"], c["v8"], c["dq"], c["dk"], c["dv"],
+                                 c["scale"], c["causal"], c["kpm"], **kw)
+
+
+def pin_fp8_attention_on_library_values():
+    """The FP8 oracle is the definition on descale * value: values widened by
+    torch's float8_e4m3fn and scaled per (b, h) here give the same result."""
+    for seed, causal, mask in ((4501, False, "none"), (4502, True, "lengths"), (4503, False, "random")):
+        c = _fp8_case(seed, 2, 3, 37, 53, 16, causal=causal, mask=mask)
+        vals = {}
+        for n in ("q", "k", "v"):
+            t = torch.from_numpy(c[n + "8"].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+            ds = c["d" + n].astype(np.float64)
+            vals[n] = t * ds[:, :, None, None]
+        assert len(np.unique(c["dq"])) == 6, "per-head descales must differ for this pin"
+        O_ref, lse_ref = A.attention_fp64(vals["q"], vals["k"], vals["v"], c["scale"], causal, c["kpm"])
+        O, lse = run_fp8(c)
+        close(O, O_ref, 1e-13, "fp8 O vs definition on library-decoded values")
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(lse), fin)
+        close(lse[fin], lse_ref[fin], 1e-13, "fp8 lse vs definition")
+
+
+def pin_fp8_descale_identities():
+    """Doubling descale_v doubles O and leaves lse; doubling descale_q is the same
+    as doubling the scale; changing one head's descale_k changes only that head."""
+    c = _fp8_case(4504, 2, 2, 29, 41, 16, causal=True)
+    O, lse = run_fp8(c)
+    c2 = dict(c, dv=c["dv"] * np.float32(2))
+    O2, lse2 = run_fp8(c2)
+    close(O2, 2 * O, 1e-13, "descale_v doubled")
+    close(lse2, lse, 1e-13, "lse independent of descale_v")
+    c3 = dict(c, dq=c["dq"] * np.float32(2))
+    O3, lse3 = run_fp8(c3)
+    O4, lse4 = run_fp8(dict(c, scale=2 * c["scale"]))
+    close(O3, O4, 1e-13, "descale_q doubled vs scale doubled")
+    close(lse3, lse4, 1e-13, "lse: descale_q doubled vs scale doubled")
+    dk = c["dk"].copy()
+    dk[1, 0] *= np.float32(3)
+    O5, _ = run_fp8(dict(c, dk=dk))
+    changed = np.abs(O5 - O).max(axis=(2, 3)) > 1e-9
+    assert changed.tolist() == [[False, False], [True, False]], changed
+
+
 PINS = [
     pin_worked_example,
     pin_oracle_materialises_closed_form,
@@ -439,4 +527,8 @@ PINS = [
     pin_backward_torch_autograd,
     pin_backward_finite_differences,
     pin_backward_identities,
+    pin_e4m3_decode_against_torch,
+    pin_e4m3_decode_closed_forms,
+    pin_fp8_attention_on_library_values,
+    pin_fp8_descale_identities,
 ]

@@ -175,3 +175,53 @@ def test_backward_mutant_is_caught(name, monkeypatch):
         except Exception as e:
             failed.append((pin.__name__, type(e).__name__))
     assert failed, f"mutant {name} passed every pin"
+
+
+import oracle.fp8 as F8  # noqa: E402
+
+ORIG_DEC = F8.e4m3_to_fp64
+ORIG_DEQ = F8.dequantize_heads
+
+
+def _dec_fields(bias=7, mant_div=8.0, sub_as_normal=False, signed=True):
+    def f(bits):
+        b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+        s = np.where((b >> 7) & 1, -1.0, 1.0) if signed else 1.0
+        e = (b >> 3) & 0xF
+        m = (b & 7).astype(np.float64)
+        if sub_as_normal:
+            mag = (1.0 + m / mant_div) * np.exp2(np.maximum(e, 1) - float(bias))
+        else:
+            mag = np.where(e == 0, (m / mant_div) * 2.0 ** (1 - bias),
+                           (1.0 + m / mant_div) * np.exp2(e - float(bias)))
+        return np.where((e == 15) & (m == 7), np.nan, s * mag)
+    return f
+
+
+FP8_MUTANTS = {
+    "e4m3_bias_8": ("e4m3_to_fp64", _dec_fields(bias=8)),
+    "e4m3_mantissa_quarters": ("e4m3_to_fp64", _dec_fields(mant_div=4.0)),
+    "e4m3_subnormals_as_normals": ("e4m3_to_fp64", _dec_fields(sub_as_normal=True)),
+    "e4m3_sign_dropped": ("e4m3_to_fp64", _dec_fields(signed=False)),
+    "descale_ignored": ("dequantize_heads", lambda bits, ds: ORIG_DEQ(bits, None)),
+    "descale_batch_head_swapped": (
+        "dequantize_heads",
+        lambda bits, ds: ORIG_DEQ(bits, None if ds is None else
+                                  np.asarray(ds).T.reshape(np.asarray(ds).shape))),
+    "descale_squared": ("dequantize_heads",
+                        lambda bits, ds: ORIG_DEQ(bits, None if ds is None else np.asarray(ds) ** 2)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(name, monkeypatch):
+    attr, fn = FP8_MUTANTS[name]
+    monkeypatch.setattr(F8, attr, fn)
+    failed = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception as e:
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"

@@ -47,3 +47,31 @@ def test_k_multiplier_applied_before_rounding():
 def test_flop_formula():
     assert WORKLOADS[2].flops() == 4 * 32 * 8192 * 8192 * 128 / 2
     assert WORKLOADS[3].flops() == 4 * 4 * 16 * 2048 * 2048 * 64
+
+
+def test_e4m3_rounding_matches_torch():
+    """round_to_e4m3 (input generation) rounds like torch's float8_e4m3fn cast
+    (round to nearest even) inside the finite range and saturates outside it."""
+    from workloads import round_to_e4m3
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(50000) * np.exp2(rng.uniform(-14, 10, 50000))).astype(np.float32)
+    x = np.concatenate([x, np.array([0.0, -0.0, 448.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10,
+                                     2.0 ** -11, 464.0, 1e9, -1e9], np.float32)])
+    ref = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(round_to_e4m3(x), ref)
+
+
+def test_quantize_heads_uses_full_range_per_head():
+    from workloads import quantize_heads_e4m3
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((2, 3, 40, 16)).astype(np.float32)
+    x[1, 2] *= 0  # an all-zero head keeps descale 1
+    bits, ds = quantize_heads_e4m3(x)
+    assert bits.dtype == np.uint8 and ds.shape == (2, 3) and ds[1, 2] == 1.0
+    mags = bits & 0x7F
+    for b in range(2):
+        for h in range(3):
+            if (b, h) != (1, 2):
+                assert mags[b, h].max() == 0x7E  # the head's max maps to 448
+    vals = torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).float().numpy() * ds[:, :, None, None]
+    assert np.abs(vals - x).max() <= 2.0 ** -4 * np.abs(x).max() + 1e-7

@@ -11,6 +11,11 @@ example of 32,000-token training sequences for a 7B model (s = 32768, H = 32,
 d = 128 stands in for that layer). Every tensor is drawn from N(0, 1) in
 float32 with NumPy's PCG64, then rounded to bfloat16 with round-to-nearest-even,
 so the oracle and the kernel see bit-identical values.
+
+For the 8-bit-float forward, the same float32 draws are quantised per
+(batch item, head) to OCP E4M3 codes with a float32 descale factor each
+(``quantize_heads_e4m3``); the rounding is a number-format conversion, not a
+step of the attention method.
 """
 from __future__ import annotations
 
@@ -27,6 +32,8 @@ __all__ = [
     "SPLIT_WORKLOADS",
     "round_to_bf16",
     "bf16_bits_to_f32",
+    "round_to_e4m3",
+    "quantize_heads_e4m3",
     "generate",
     "random_case",
     "padding_mask_from_lengths",
@@ -57,6 +64,49 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Widen bfloat16 bit patterns (uint16) to the exactly equal float32 values."""
     return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the OCP 8-bit float E4M3 (1 sign, 4 exponent bits
+    with bias 7, 3 mantissa bits, subnormals, no infinities, largest finite
+    magnitude 448) with round-to-nearest-even, saturating at +-448.
+
+    Returns uint8 bit patterns; NaN becomes 0x7F. Used only to make FP8 inputs.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)
+    a[np.isnan(a)] = 0.0
+    # a = f * 2**E with f in [0.5, 1): the binade exponent is E - 1; below 2**-6
+    # every value is on the subnormal grid of step 2**-9
+    _, E = np.frexp(a)
+    e = np.maximum(E.astype(np.float64) - 1.0, -6.0)
+    step = np.exp2(e - 3.0)
+    r = np.minimum(np.rint(a / step) * step, 448.0)  # may carry into the next binade
+    _, E2 = np.frexp(r)
+    e2 = E2.astype(np.float64) - 1.0
+    sub = r < 2.0 ** -6
+    code_sub = np.rint(r / 2.0 ** -9)
+    e2n = np.maximum(e2, -6.0)
+    code_n = (e2n + 7.0) * 8.0 + np.rint((r / np.exp2(e2n) - 1.0) * 8.0)
+    bits = np.where(sub, code_sub, code_n).astype(np.uint8)
+    bits |= (np.signbit(x).astype(np.uint8) << np.uint8(7))
+    bits[np.isnan(x)] = np.uint8(0x7F)
+    return bits
+
+
+def quantize_heads_e4m3(x: np.ndarray) -> tuple:
+    """Per-(b, h) E4M3 quantisation of a float32 [B, H, s, d] tensor.
+
+    descale[b, h] = max|x[b, h]| / 448 (1 for an all-zero head), and the
+    returned bits are round_to_e4m3(x / descale): the decoded values times
+    descale approximate x, and each head uses the format's full range.
+    Returns (bits uint8 [B, H, s, d], descale float32 [B, H]).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=(2, 3)) if x.size else np.zeros(x.shape[:2], np.float32)
+    descale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    bits = round_to_e4m3(x / descale[:, :, None, None])
+    return bits, descale
 
 
 def scale_for(d: int) -> np.float32:
