@@ -23,7 +23,10 @@ key-split entry point (attn_fwd_split: n key chunks, then their merge) on a
 shape from workloads.SPLIT_WORKLOADS; a workload with key padding also reports
 useful_tflops (FLOPs on the visible keys only); --calibrate-copy adds one plain device copy
 of known size after the timed region, so a counter profile of this command also
-holds the reference that scales FETCH_SIZE / WRITE_SIZE to bytes.
+holds the reference that scales FETCH_SIZE / WRITE_SIZE to bytes; --fp8
+times the 8-bit-float forward (attn_fwd_fp8) on the same workload, its inputs
+quantised per (batch item, head) to OCP E4M3 codes with float32 descale
+factors, against the dense FP8 MFMA peak.
 """
 import argparse
 import json
@@ -39,6 +42,8 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s at 1 MI355X (s=4096–32768) + % of bf16 MFMA peak"
 # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+# MI355X dense FP8 MFMA: twice the bf16 rate
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
 COPY_BYTES = 1 << 30
 KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_fwd.hip")
 
@@ -71,6 +76,9 @@ def parse():
                     help="time the backward pass (attn_bwd) of the workload instead; FLOPs "
                          "counted as 2.5x the forward's (five products of its size, one of "
                          "them the recomputed scores)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the 8-bit-float forward (attn_fwd_fp8) on E4M3-quantised "
+                         "inputs of the workload instead")
     ap.add_argument("--splits", type=int, default=4,
                     help="key chunks for --split-workload (1 = the plain launch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -80,12 +88,13 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, g, target_s, backward=False):
+def cpu_baseline(w, g, target_s, backward=False, fp8=None):
     """Time the oracle on whole heads of the same workload until ~target_s
-    (its gradients, with a seeded output gradient, for the backward pass)."""
+    (its gradients, with a seeded output gradient, for the backward pass; the
+    E4M3 oracle on the quantised inputs `fp8` for the 8-bit-float forward)."""
     import numpy as np
 
-    from oracle import attention_backward_fp64, attention_fp64
+    from oracle import attention_backward_fp64, attention_fp64, attention_fp8_fp64
     from workloads import bf16_bits_to_f32
 
     threads = os.cpu_count()
@@ -103,7 +112,13 @@ def cpu_baseline(w, g, target_s, backward=False):
         for h in range(w.H):
             q, k, v = (bf16_bits_to_f32(g[n][b:b + 1, h:h + 1]) for n in ("q", "k", "v"))
             kpm = None if g["kpm"] is None else g["kpm"][b:b + 1]
-            if backward:
+            if fp8 is not None:
+                sl = (slice(b, b + 1), slice(h, h + 1))
+                t0 = time.perf_counter()
+                attention_fp8_fp64(*(fp8[n + "8"][sl] for n in ("q", "k", "v")),
+                                   *(fp8["d" + n][sl] for n in ("q", "k", "v")),
+                                   float(g["scale"]), w.causal, kpm)
+            elif backward:
                 dout = rng.standard_normal(q.shape)
                 t0 = time.perf_counter()
                 attention_backward_fp64(q, k, v, dout, float(g["scale"]), w.causal, kpm)
@@ -121,7 +136,8 @@ def cpu_baseline(w, g, target_s, backward=False):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"float64 NumPy oracle{' gradients' if backward else ''} (materialises each head's s x s scores, row blocks "
+        "sample": (f"float64 NumPy oracle{' gradients' if backward else ''}"
+                   f"{' on E4M3 inputs' if fp8 is not None else ''} (materialises each head's s x s scores, row blocks "
                    f"of 2048) on {heads} of {w.B * w.H} heads of {w.name}: {spent:.1f} s on "
                    f"{threads} BLAS threads, {platform.processor() or platform.machine()}; "
                    f"FLOPs counted with the metric formula"),
@@ -158,7 +174,21 @@ def main():
     args = (q, k, v, out, lse, w.B, w.H, w.s_q, w.s_k, w.d, float(g["scale"]), w.causal, kpm,
             stream.cuda_stream)
 
-    if a.backward:
+    fp8 = None
+    if a.fp8:
+        from workloads import bf16_bits_to_f32, quantize_heads_e4m3
+        fp8 = {}
+        for n in ("q", "k", "v"):
+            fp8[n + "8"], fp8["d" + n] = quantize_heads_e4m3(bf16_bits_to_f32(g[n]))
+        q8, k8, v8 = (torch.from_numpy(fp8[n + "8"]).to(dev) for n in ("q", "k", "v"))
+        dq8, dk8, dv8 = (torch.from_numpy(fp8["d" + n]).to(dev) for n in ("q", "k", "v"))
+
+        def step():
+            st = E.attn_fwd_fp8(q8, k8, v8, dq8, dk8, dv8, out, lse, w.B, w.H, w.s_q, w.s_k, w.d,
+                                float(g["scale"]), w.causal, kpm, stream.cuda_stream)
+            if st != E.ATTN_OK:
+                raise E.AttnError(st)
+    elif a.backward:
         # forward outputs and a seeded output gradient, before any timing
         st = E.attn_fwd(*args)
         if st != E.ATTN_OK:
@@ -222,14 +252,17 @@ def main():
         torch.cuda.synchronize()
 
     flops = w.flops() * (2.5 if a.backward else 1.0)
-    if a.backward:  # read q, out, dout, k, v, lse; write dq, dk, dv
+    if a.fp8:  # E4M3 q, k, v (one byte each) and the descales read; bf16 out, lse written
+        algorithmic_bytes = w.B * w.H * (w.s_q + 2 * w.s_k) * w.d + 12 * w.B * w.H \
+            + 2 * w.B * w.H * w.s_q * w.d + 4 * w.B * w.H * w.s_q
+    elif a.backward:  # read q, out, dout, k, v, lse; write dq, dk, dv
         algorithmic_bytes = 2 * w.B * w.H * (3 * w.s_q + 2 * w.s_k) * w.d + 4 * w.B * w.H * w.s_q \
             + 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d
     else:
         algorithmic_bytes = 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d + 2 * w.B * w.H * w.s_q * w.d \
             + 4 * w.B * w.H * w.s_q
     traffic, traffic_detail = None, {"algorithmic_bytes": algorithmic_bytes}
-    measured = None if (a.backward or split) else MEASURED_TRAFFIC.get(w.name)
+    measured = None if (a.backward or split or a.fp8) else MEASURED_TRAFFIC.get(w.name)
     if measured is not None:
         import hashlib
         with open(KERNEL_SOURCE, "rb") as f:
@@ -241,6 +274,7 @@ def main():
                                   source_sha256=current)
     value = flops * a.steps / wall / 1e12
     achieved = flops / (kern_avg_ms * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if a.fp8 else PEAK_BF16_TFLOPS
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -262,19 +296,27 @@ def main():
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
-            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "peak": round(peak, 1),
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "traffic_unit": "bytes per launch",
             "traffic_detail": traffic_detail,
-            "kernel": ("attn_bwd_dq_kernel + attn_bwd_dkv_kernel" if a.backward
+            "kernel": ("attn_fwd_fp8_kernel" if a.fp8
+                       else "attn_bwd_dq_kernel + attn_bwd_dkv_kernel" if a.backward
                        else "attn_fwd_kernel (key-split) + attn_merge_kernel" if split
                        else "attn_fwd_kernel"),
             "kernel_avg_ms": round(kern_avg_ms, 5),
             "kernel_min_ms": round(min(kern_ms), 5),
         },
     }
+    if a.fp8:
+        res["config"]["entry_point"] = "attn_fwd_fp8"
+        res["config"]["inputs"] = "OCP E4M3 codes, per-(b, h) float32 descale"
+        res["metric"] = METRIC.replace("% of bf16 MFMA peak", "% of FP8 MFMA peak") + " (FP8 forward)"
+        res["dtype"] = "fp8-e4m3 products, fp32 accumulate, bf16 out"
+        res["pct_of_fp8_peak"] = round(100.0 * value / PEAK_FP8_TFLOPS, 2)
+        del res["pct_of_bf16_peak"]
     if a.backward:
         res["config"]["pass"] = "backward"
         res["metric"] = METRIC + " (backward pass: dq, dk, dv)"
@@ -287,7 +329,7 @@ def main():
         useful = sum(4.0 * w.H * w.s_q * int(n) * w.d for n in lengths)
         res["useful_tflops"] = round(useful * a.steps / wall / 1e12, 2)
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, g, a.cpu_seconds, backward=a.backward)
+        res["cpu_baseline"] = cpu_baseline(w, g, a.cpu_seconds, backward=a.backward, fp8=fp8)
     print(json.dumps(res), flush=True)
 
 

@@ -18,7 +18,8 @@ __all__ = [
     "ATTN_ERR_ALIAS", "ATTN_ERR_SCALE", "ATTN_ERR_LAUNCH", "ATTN_ERR_WORKSPACE", "AttnError",
     "load_library", "attn_fwd", "attn_fwd_validate", "attn_fwd_split",
     "attn_fwd_split_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
-    "attn_last_hip_error", "fwd", "fwd_split", "bwd", "LIB_PATH",
+    "attn_last_hip_error", "attn_fwd_fp8", "attn_fwd_fp8_validate", "fwd", "fwd_split", "bwd",
+    "fwd_fp8", "LIB_PATH",
 ]
 
 ATTN_OK = 0
@@ -76,6 +77,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_bwd_workspace_bytes.restype = i64
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                 ctypes.c_float, ctypes.c_int, vp, vp]
+    lib.attn_fwd_fp8.restype = ctypes.c_int
+    lib.attn_fwd_fp8_validate.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                          i64, ctypes.c_float, ctypes.c_int, vp]
+    lib.attn_fwd_fp8_validate.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -137,6 +144,24 @@ def attn_bwd_workspace_bytes(B: int, H: int, s_q: int) -> int:
     return load_library().attn_bwd_workspace_bytes(B, H, s_q)
 
 
+def attn_fwd_fp8(q, k, v, descale_q, descale_k, descale_v, out, lse, B: int, H: int, s_q: int,
+                 s_k: int, d: int, scale: float, causal: bool, key_padding_mask, stream) -> int:
+    """The C entry point attn_fwd_fp8 with the same arguments."""
+    return load_library().attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(descale_q),
+                                       _ptr(descale_k), _ptr(descale_v), _ptr(out), _ptr(lse),
+                                       B, H, s_q, s_k, d, float(scale), 1 if causal else 0,
+                                       _ptr(key_padding_mask), stream)
+
+
+def attn_fwd_fp8_validate(q, k, v, descale_q, descale_k, descale_v, out, lse, B: int, H: int,
+                          s_q: int, s_k: int, d: int, scale: float, causal: bool,
+                          key_padding_mask) -> int:
+    return load_library().attn_fwd_fp8_validate(_ptr(q), _ptr(k), _ptr(v), _ptr(descale_q),
+                                                _ptr(descale_k), _ptr(descale_v), _ptr(out),
+                                                _ptr(lse), B, H, s_q, s_k, d, float(scale),
+                                                1 if causal else 0, _ptr(key_padding_mask))
+
+
 def attn_status_str(status: int) -> str:
     return load_library().attn_status_str(status).decode()
 
@@ -145,12 +170,13 @@ def attn_last_hip_error() -> int:
     return load_library().attn_last_hip_error()
 
 
-def _check_inputs(q, k, v, key_padding_mask):
+def _check_inputs(q, k, v, key_padding_mask, dtypes=None):
     import torch
 
+    dtypes = dtypes or (torch.bfloat16,)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 4:
-            raise TypeError(f"{name} must be a 4-D bfloat16 torch tensor")
+        if not isinstance(t, torch.Tensor) or t.dtype not in dtypes or t.dim() != 4:
+            raise TypeError(f"{name} must be a 4-D torch tensor of dtype {' or '.join(map(str, dtypes))}")
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
     B, H, s_q, d = q.shape
@@ -254,3 +280,36 @@ def bwd(q, k, v, out, dout, lse, *, causal: bool = False, key_padding_mask=None,
     if st != ATTN_OK:
         raise AttnError(st)
     return dq, dk, dv
+
+
+def fwd_fp8(q, k, v, *, descale_q=None, descale_k=None, descale_v=None, causal: bool = False,
+            key_padding_mask=None, scale: Optional[float] = None, out=None,
+            lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Attention forward over OCP E4M3 inputs (attn_fwd_fp8): q [B,H,s_q,d],
+    k/v [B,H,s_k,d] contiguous device tensors of dtype torch.float8_e4m3fn or
+    uint8 (the codes); descale_* None or float32 [B, H] device tensors (the
+    real value of a code is descale times its E4M3 value). Returns (out bf16
+    [B,H,s_q,d], lse float32 [B,H,s_q]) on torch's current stream."""
+    import torch
+
+    B, H, s_q, s_k, d = _check_inputs(q, k, v, key_padding_mask,
+                                      (torch.float8_e4m3fn, torch.uint8))
+    for name, t in (("descale_q", descale_q), ("descale_k", descale_k), ("descale_v", descale_v)):
+        if t is None:
+            continue
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.numel() != B * H
+                or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor of {B * H} elements")
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(q.device):
+        if out is None:
+            out = torch.empty((B, H, s_q, d), dtype=torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, H, s_q), dtype=torch.float32, device=q.device)
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_fwd_fp8(q, k, v, descale_q, descale_k, descale_v, out, lse, B, H, s_q, s_k, d,
+                          scale, causal, key_padding_mask, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, lse

@@ -7,7 +7,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", n) for n in ("attn_fwd.hip", "attn_bwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libattn.so")
 
@@ -30,7 +30,7 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile csrc/attn_fwd.hip and csrc/attn_bwd.hip into exact_attention_44_amd/libattn.so."""
+    """Compile the csrc/*.hip sources into exact_attention_44_amd/libattn.so."""
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

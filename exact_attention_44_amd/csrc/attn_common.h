@@ -17,6 +17,8 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));  // 32 E4M3 codes
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 // hipError_t behind the calling thread's last ATTN_ERR_LAUNCH (any entry point)
 __attribute__((visibility("hidden"))) inline thread_local int g_last_hip_error = 0;
@@ -36,6 +38,30 @@ __device__ __forceinline__ int key_of_row(int m) {
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x64 product of OCP E4M3 operands with float32 accumulation. Lane L
+// holds row (A) or column (B) L % 32 and the 32 consecutive k values
+// 32 * (L / 32) .. +31, one code per byte, lowest k in the lowest byte.
+__device__ __forceinline__ f32x16_t mfma_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Four float32 values rounded to E4M3 codes (nearest even; magnitudes from
+// 480 up give NaN, so callers keep them below that), first value in the
+// lowest byte.
+__device__ __forceinline__ uint32_t pack_e4m3(float x0, float x1, float x2, float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return (uint32_t)w;
+}
+
+// LDS transpose read of 8-bit elements: within each group of 16 lanes, byte
+// k (0..7) of lane i comes from the address given by lane 2k + (i >= 8) of
+// the group, plus (i & 7). The eight even lanes' 8-byte rows are transposed
+// into lanes 0..7 and the odd lanes' rows into lanes 8..15.
+__device__ __forceinline__ i32x2_t lds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)p);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {

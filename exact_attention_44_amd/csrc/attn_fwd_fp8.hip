@@ -1,0 +1,573 @@
+// attn_fwd_fp8.hip - fused attention forward over 8-bit floating-point inputs
+// for gfx950 (CDNA4), and its C ABI.
+//
+// Method: the same tiled walk with online softmax as the bf16 forward
+// (news.hamidun.com glossary "Flash attention", second paragraph; onecalc.app
+// "Attention memory", section "FlashAttention"). The glossary's second
+// paragraph names FP8 precision as the third version's addition. Here Q, K and
+// V arrive as OCP E4M3 codes with one float32 descale factor per (batch item,
+// head) each, both products run on the 8-bit matrix cores
+// (v_mfma_f32_32x32x64_f8f6f4, float32 accumulation), and the softmax weights
+// are rounded to E4M3 for the value product. The running max, row sums and
+// the output accumulator stay float32; the output is bf16.
+//
+// Decomposition and schedule follow the bf16 kernel: one workgroup per
+// (b, h, 256 query rows), 8 waves of 32 rows, waves w and w + 4 on one SIMD,
+// the two groups of four alternating matrix phases (value product of the
+// previous tile, score product of this one) and vector phases (masks and
+// softmax), separated by workgroup barriers.
+//
+// Operand layouts. Scores are computed transposed, S^T = K Q^T: A = 32 keys x
+// 64 features (K rows in their natural order), B = 64 features x 32 queries
+// (Q in registers). In the 32x32 accumulator lane L holds query L % 32 and the
+// 16 keys 8a + 4h + b (a, b in 0..3, h = L / 32) of each 32-key block. The
+// value product O^T += V^T P^T takes a whole 64-key tile in one k-step: the
+// B operand is lane L's 32 weights, byte j = register j % 16 of key block
+// j / 16, so slot (h, j) of the k axis is key
+//   key(h, j) = 32 (j / 16) + 8 ((j % 16) / 4) + 4 h + j % 4,
+// and the A operand (V^T: 32 feature rows x the same 64 key slots) is read
+// from the row-major V tile with LDS transpose reads that gather, for each
+// lane's feature, the bytes of exactly those keys.
+//
+// LDS per tile: K row-major in key order, rows padded to D + 16 bytes (the 16
+// lanes of each 16-byte fragment read hit distinct banks). V row-major in
+// k-slot order: LDS row 32 h + j holds key(h, j), rows padded to D + 32
+// bytes, so each transpose read covers eight consecutive rows whose starts
+// fall in distinct 8-bank groups (conflict-free) and every read address is a
+// per-lane base plus compile-time offsets. Both tiles arrive by buffer loads
+// that write LDS directly.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "attn_common.h"
+
+namespace {
+
+using namespace attn_detail;
+
+struct Fp8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* dsq;  // descale factors [B*H] or null (1)
+  const float* dsk;
+  const float* dsv;
+  uint16_t* out;
+  float* lse;
+  const uint8_t* kpm;
+  int s_q, s_k, H, BH, n_qt;
+  float scale;
+};
+
+// Key (within the 64-key tile) at slot j of lane half h of the value
+// product's k axis: the key that score accumulator register j % 16 of key
+// block j / 16 holds in that lane half.
+__device__ __forceinline__ int key_of_slot(int h, int j) {
+  return 32 * (j >> 4) + 8 * ((j & 15) >> 2) + 4 * h + (j & 3);
+}
+
+template <int D, bool CAUSAL, bool PADMASK>
+__global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
+  constexpr int NT = 512;             // 8 waves: two ping-pong groups of 4
+  constexpr int BR = 256;             // query rows per workgroup, 32 per wave
+  constexpr int BC = 64;              // keys per tile (one k-step of the value product)
+  constexpr int KB = BC / 32;         // 32-key blocks of the score tile
+  constexpr int DK = D / 64;          // k-steps of the score product
+  constexpr int DB = D / 32;          // 32-feature blocks of the output
+  constexpr int KU = D / 16;          // 16-byte units per K or V row
+  constexpr int KS = D + 16;          // K row stride (bytes)
+  constexpr int VS = D + 32;          // V row stride (bytes)
+  constexpr int K_BYTES = BC * KS;
+  constexpr int V_BYTES = BC * VS;
+  constexpr int BUF_BYTES = K_BYTES + V_BYTES;
+  constexpr int NBUF = 4;
+  // Each group stages half of a tile's LDS rows: K rows 32 grp .. +31 (keys
+  // 32 grp ..) and V rows 32 grp .. +31 (the keys of lane half grp). A half is
+  // 32 padded rows of 16-byte slots written by DMA instructions of 64
+  // consecutive slots each; the last instruction overlaps its predecessor
+  // (the overlap is written twice with the same data) and a padding slot
+  // receives a copy of its row's first 16 bytes.
+  constexpr int ROW_SLOTS = KS / 16;
+  constexpr int K_SLOTS = 32 * ROW_SLOTS;
+  constexpr int K_DMA = (K_SLOTS + 63) / 64;
+  constexpr int K_DMA_W = (K_DMA + 3) / 4;
+  constexpr int VROW_SLOTS = VS / 16;
+  constexpr int V_SLOTS = 32 * VROW_SLOTS;
+  constexpr int V_DMA = (V_SLOTS + 63) / 64;
+  constexpr int V_DMA_W = (V_DMA + 3) / 4;
+  static_assert(K_SLOTS >= 64 && V_SLOTS >= 64, "a half tile must fill one DMA instruction");
+  // Weights are taken against a reference max that can lag the true one;
+  // their float32 tile sum bounds every weight, and E4M3 conversion turns
+  // magnitudes from 480 up into NaN, so a tile whose sum exceeds 256 is
+  // recomputed against the true max.
+  constexpr float kSumLimit = 256.f;
+
+  __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF_BYTES];
+  __shared__ int lds_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv >> 2;
+  const int hl = lane >> 5;
+  const int ln = lane & 31;
+
+  const int L = blockIdx.x;
+  const int qt = CAUSAL ? (p.n_qt - 1 - L / p.BH) : (L / p.BH);
+  const int bh = L % p.BH;
+  const int b = bh / p.H;
+  const int q0 = qt * BR;
+  const int s_q = p.s_q, s_k = p.s_k;
+
+  // Per-head score scale: scores enter exp2 as (q8 . k8) * c with
+  // c = |scale * dq * dk| * log2(e); a negative product negates Q (the sign
+  // bit of each code), a zero one zeroes Q.
+  const float dq = p.dsq ? p.dsq[bh] : 1.f;
+  const float dk = p.dsk ? p.dsk[bh] : 1.f;
+  const float dv = p.dsv ? p.dsv[bh] : 1.f;
+  const float cs = p.scale * dq * dk;
+  const float cs_abs = fabsf(cs);
+  const bool zero_scale = cs_abs < 1e-30f;  // NaN propagates
+  const uint32_t q_and = zero_scale ? 0u : ~0u;
+  const uint32_t q_xor = (!zero_scale && cs < 0.f) ? 0x80808080u : 0u;
+  const float c = zero_scale ? kLog2e : cs_abs * kLog2e;
+  const float scale_abs = zero_scale ? 0.f : cs_abs;
+
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (int64_t)bh * s_q * D, (uint32_t)s_q * D);
+  const uint8_t* kg = p.k + (int64_t)bh * s_k * D;
+  const uint8_t* vg = p.v + (int64_t)bh * s_k * D;
+  const uint8_t* mg = PADMASK ? p.kpm + (int64_t)b * s_k : nullptr;
+
+  // ---- keys this tile can see (causal: up to the last query row; padding:
+  // up to the last key that is not padded)
+  int kend = s_k;
+  if (CAUSAL) kend = min(kend, q0 + BR);
+  if (PADMASK) {
+    if (tid == 0) lds_last = -1;
+    __syncthreads();
+    int last = -1;
+    for (int cend = s_k; cend > 0; cend -= NT * 4) {
+      const int cbeg = max(0, cend - NT * 4);
+      int best = -1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = cbeg + tid * 4 + i;
+        if (j < cend && mg[j] == 0) best = j;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
+      if (lane == 0 && best >= 0) atomicMax(&lds_last, best);
+      __syncthreads();
+      const int found = lds_last;
+      __syncthreads();
+      if (found >= 0) {
+        last = found;
+        break;
+      }
+    }
+    kend = min(kend, last + 1);
+  }
+  const int n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
+
+  // ---- Q (B operand of the score product): lane holds query qlo + ln,
+  // features 64 kk + 32 hl .. +31
+  const int qlo = q0 + 32 * wv;
+  i32x8_t qf[DK];
+  {
+    const uint32_t row = (uint32_t)(qlo + ln);
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u32x4_t x = load16(rq, row * D + 64 * kk + 32 * hl + 16 * u);
+        x = (x & q_and) ^ q_xor;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[kk][4 * u + e] = (int)x[e];
+      }
+    }
+  }
+
+  // ---- staging of this group's half (keys 32 grp .. 32 grp + 31) of a tile
+  const int wg = wv & 3;
+  uint32_t k_voff[K_DMA_W];
+#pragma unroll
+  for (int i = 0; i < K_DMA_W; ++i) {
+    const int j = wg + 4 * i;
+    const int slot = min(64 * j, K_SLOTS - 64) + lane;
+    const int row = 32 * grp + slot / ROW_SLOTS, un = slot % ROW_SLOTS;
+    k_voff[i] = (uint32_t)(row * D + (un < KU ? 16 * un : 0));
+  }
+  uint32_t v_voff[V_DMA_W];
+#pragma unroll
+  for (int i = 0; i < V_DMA_W; ++i) {
+    const int j = wg + 4 * i;
+    const int slot = min(64 * j, V_SLOTS - 64) + lane;
+    const int key = key_of_slot(grp, slot / VROW_SLOTS), un = slot % VROW_SLOTS;
+    v_voff[i] = (uint32_t)(key * D + (un < KU ? 16 * un : 0));
+  }
+  auto dma_k = [&](int u) {
+    const int j0 = u * BC;
+    const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(kg + (int64_t)j0 * D, rest);
+    char* dst = lds + (u % NBUF) * BUF_BYTES + grp * K_SLOTS * 16;
+#pragma unroll
+    for (int i = 0; i < K_DMA_W; ++i) {
+      const int j = wg + 4 * i;
+      if (j < K_DMA) load16_to_lds(r, dst + min(64 * j, K_SLOTS - 64) * 16, k_voff[i]);
+    }
+  };
+  auto dma_v = [&](int u) {
+    const int j0 = u * BC;
+    const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(vg + (int64_t)j0 * D, rest);
+    char* dst = lds + (u % NBUF) * BUF_BYTES + K_BYTES + grp * V_SLOTS * 16;
+#pragma unroll
+    for (int i = 0; i < V_DMA_W; ++i) {
+      const int j = wg + 4 * i;
+      if (j < V_DMA) load16_to_lds(r, dst + min(64 * j, V_SLOTS - 64) * 16, v_voff[i]);
+    }
+  };
+
+  // ---- per-wave running state
+  f32x16_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t sc[KB];
+  i32x8_t pf;              // E4M3 weights of the tile between its two phases
+  uint32_t mbyte = 1u;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16_t{};
+
+  const int k_lane_off = ln * KS + hl * 32;
+  // Transpose-read address of the value product's A operand. Lane L (group
+  // G = L / 16, x = L % 16, half h = G / 2) reads, for byte block tb and
+  // feature block db, LDS row 32 h + 8 tb + x / 2 (key key(h, 8 tb + x / 2))
+  // at features 32 db + 16 (G & 1) + 8 (x & 1) .. +7; the transpose hands
+  // lane L the bytes of its own feature 32 db + L % 32 for the keys of slots
+  // 8 tb .. 8 tb + 7 of its half.
+  const int v_lane_off = (32 * (lane >> 5) + ((lane & 15) >> 1)) * VS + 16 * ((lane >> 4) & 1) +
+                         8 * (lane & 1);
+  auto v_read = [&](int t, int i) -> i32x2_t {
+    // read i of tile t's value product: feature block i / 4, byte block i % 4
+    const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + v_lane_off;
+    const int db = i >> 2, tb = i & 3;
+    return lds_read_tr8(vl + 8 * tb * VS + 32 * db);
+  };
+
+  constexpr int N_VR = 4 * DB;  // transpose reads per value product
+  constexpr int LA = 8;         // of them issued before the M step's barrier
+  static_assert(LA <= N_VR, "prefetched reads must belong to the value product");
+  i32x2_t vpre[LA];
+  // M step, first half: O^T += V_t^T P(t)^T.
+  auto pv = [&](int t) {
+    i32x2_t vr[N_VR];
+#pragma unroll
+    for (int i = 0; i < N_VR; ++i) vr[i] = i < LA ? vpre[i < LA ? i : 0] : v_read(t, i);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      i32x8_t a;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        a[2 * tb] = vr[4 * db + tb][0];
+        a[2 * tb + 1] = vr[4 * db + tb][1];
+      }
+      o[db] = mfma_e4m3(a, pf, o[db]);
+    }
+  };
+  // M step, second half: S(t)^T = K_t Q^T.
+  auto qk = [&](int t) {
+    const char* kl = lds + (t % NBUF) * BUF_BYTES + k_lane_off;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      i32x8_t a[DK];
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4_t x = *(const u32x4_t*)(kl + kb * 32 * KS + kk * 64 + 16 * u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[kk][4 * u + e] = (int)x[e];
+        }
+      }
+      f32x16_t acc = {};
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk) acc = mfma_e4m3(a[kk], qf[kk], acc);
+      sc[kb] = acc;
+    }
+    if (PADMASK) {
+      const int key = t * BC + lane;
+      mbyte = key < s_k ? (uint32_t)mg[key] : 1u;
+    }
+  };
+  auto m_step = [&](int tp, int tq) {
+    __builtin_amdgcn_s_setprio(2);
+    pv(tp);
+    qk(tq);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // V step: staging of later tiles, then masks and online softmax of S(t).
+  auto vstep = [&](int t) {
+    dma_k(t + 3);
+    dma_v(t + 2);
+    const int j0 = t * BC;
+    uint64_t hid;
+    if (PADMASK) {
+      hid = __ballot(mbyte != 0u);
+    } else {
+      const int rem = s_k - j0;
+      hid = rem >= BC ? 0ull : ~((1ull << rem) - 1ull);
+    }
+    if (hid != 0ull || (CAUSAL && j0 + BC - 1 > qlo)) {
+      // register r of block kb holds key offset 32 kb + 8 (r / 4) + 4 hl + r % 4
+      const uint64_t hsh = hid >> (4 * hl);
+      const int lim = qlo + ln - j0 - 4 * hl;  // causal: visible iff offset - 4 hl <= lim
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint32_t w = (uint32_t)(hsh >> (32 * kb));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kr = 8 * (r >> 2) + (r & 3);
+          const bool hide = ((w >> kr) & 1u) || (CAUSAL && 32 * kb + kr > lim);
+          if (hide) sc[kb][r] = -INFINITY;
+        }
+      }
+    }
+    if (PADMASK ? (__ballot(m_run == -INFINITY) != 0ull) : (t == 0)) {
+      float mx = sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (m_run == -INFINITY) m_run = mx;
+    }
+    float nmc = -((m_run == -INFINITY) ? 0.f : m_run) * c;
+    auto weights = [&]() -> float {
+      float x[KB][16];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(sc[kb][r], c, nmc);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[kb][r] = __builtin_amdgcn_exp2f(x[kb][r]);
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ps[r & 3] += x[kb][r];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2, r0 = 4 * (w & 3);
+        pf[w] = (int)pack_e4m3(x[kb][r0], x[kb][r0 + 1], x[kb][r0 + 2], x[kb][r0 + 3]);
+      }
+      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+    float rs = weights();
+    if (__ballot(!(rs <= kSumLimit)) != 0ull) {
+      float mx = sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const bool none = m_new == -INFINITY;
+      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+      nmc = none ? 0.f : -m_new * c;
+      rs = weights();
+    }
+    l_run += rs;
+  };
+
+  if (n_kv > 0) {
+    dma_k(0);
+    dma_k(1);
+    dma_k(2);
+    dma_v(0);
+    dma_v(1);
+  }
+  __syncthreads();
+
+  // ---- ping-pong phases, as in the bf16 kernel. Group 0 runs
+  // QK(0) V(0) M(0,1) V(1) ... V(n-1) PV(n-1), group 1 the same one phase
+  // later. LDS buffer u % 4 holds tile u. K(u) is requested in the V steps of
+  // phases 2u - 5 (group 0) and 2u - 4 (group 1), V(u) in phases 2u - 3 and
+  // 2u - 2; the fenced barrier at the end of the requesting wave's next M
+  // step waits for them. K(u) is read by QK(u) in phases 2u, 2u + 1; V(u) by
+  // PV(u) from the end of phase 2u + 1 to phase 2u + 3. Buffer u % 4 is next
+  // written for tile u + 4: its K from phase 2u + 3, its V from phase 2u + 5.
+  auto phase_sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // After a V step: issue the first LA reads of PV(t), then a bare barrier
+  // (this step wrote no LDS through stores; its DMA is waited for at the next
+  // fenced barrier, long before the data is read).
+  auto vstep_sync = [&](int t) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) vpre[i] = v_read(t, i);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (grp == 0) {
+    if (n_kv > 0) qk(0);
+    phase_sync();
+    for (int t = 0; t < n_kv - 1; ++t) {
+      vstep(t);
+      vstep_sync(t);
+      m_step(t, t + 1);
+      phase_sync();
+    }
+    if (n_kv > 0) {
+      vstep(n_kv - 1);
+      vstep_sync(n_kv - 1);
+      pv(n_kv - 1);
+      phase_sync();
+    }
+    phase_sync();
+  } else {
+    phase_sync();
+    if (n_kv > 0) {
+      qk(0);
+      phase_sync();
+      vstep(0);
+      vstep_sync(0);
+    }
+    for (int t = 1; t < n_kv; ++t) {
+      m_step(t - 1, t);
+      phase_sync();
+      vstep(t);
+      vstep_sync(t);
+    }
+    if (n_kv > 0) pv(n_kv - 1);
+    phase_sync();
+  }
+
+  // ---- epilogue: O = dv * O^T / l, lse = m |scale dq dk| + ln(l)
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? dv * __builtin_amdgcn_rcpf(l_tot) : 0.f;
+  const int row = qlo + ln;
+  if (row < s_q) {
+    uint16_t* og = p.out + ((int64_t)bh * s_q + row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2_t w;
+        w[0] = pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
+        w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        *(u32x2_t*)(og + 32 * db + 8 * g + 4 * hl) = w;
+      }
+    }
+    if (hl == 0) {
+      p.lse[(int64_t)bh * s_q + row] =
+          l_tot > 0.f ? m_run * scale_abs + __builtin_amdgcn_logf(l_tot) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool PADMASK>
+hipError_t launch(const Fp8Params& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL, PADMASK>), dim3(grid), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_fp8_validate(const void* q, const void* k, const void* v,
+                                     const float* descale_q, const float* descale_k,
+                                     const float* descale_v, const void* out, const float* lse,
+                                     int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d,
+                                     float scale, int causal, const uint8_t* key_padding_mask) {
+  (void)causal;
+  if (B < 0 || H < 0 || s_q < 0 || s_k < 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  const int64_t kMaxSeq = (int64_t)1 << 22;
+  if (s_q > kMaxSeq || s_k > kMaxSeq) return ATTN_ERR_SHAPE;
+  if (H > 0 && B > INT32_MAX / H) return ATTN_ERR_SHAPE;
+  const int64_t BH = B * H;
+  if (BH * ((s_q + 255) / 256) > (int64_t)(UINT32_MAX / 512)) return ATTN_ERR_SHAPE;
+  if (BH == 0 || s_q == 0) return ATTN_OK;
+  if (!q || !out || !lse) return ATTN_ERR_NULL;
+  if (s_k > 0 && (!k || !v)) return ATTN_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)out) & 15u) return ATTN_ERR_ALIGN;
+  if (s_k > 0 && (((uintptr_t)k | (uintptr_t)v) & 15u)) return ATTN_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)descale_q | (uintptr_t)descale_k | (uintptr_t)descale_v) & 3u)
+    return ATTN_ERR_ALIGN;
+  const int64_t nq = BH * s_q * d, nk = BH * s_k * d, no = BH * s_q * d * 2, nl = BH * s_q * 4;
+  const int64_t nm = key_padding_mask ? B * s_k : 0, nd = BH * 4;
+  const void* ins[7] = {q, k, v, key_padding_mask, descale_q, descale_k, descale_v};
+  const int64_t ns[7] = {nq, nk, nk, nm, nd, nd, nd};
+  for (int i = 0; i < 7; ++i) {
+    if (overlaps(out, no, ins[i], ns[i]) || overlaps(lse, nl, ins[i], ns[i])) return ATTN_ERR_ALIAS;
+  }
+  if (overlaps(out, no, lse, nl)) return ATTN_ERR_ALIAS;
+  return ATTN_OK;
+}
+
+extern "C" int attn_fwd_fp8(const void* q, const void* k, const void* v, const float* descale_q,
+                            const float* descale_k, const float* descale_v, void* out, float* lse,
+                            int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d, float scale,
+                            int causal, const uint8_t* key_padding_mask, void* stream) {
+  const int st = attn_fwd_fp8_validate(q, k, v, descale_q, descale_k, descale_v, out, lse, B, H,
+                                       s_q, s_k, d, scale, causal, key_padding_mask);
+  if (st != ATTN_OK) return st;
+  if (B * H == 0 || s_q == 0) return ATTN_OK;
+  Fp8Params p = {};
+  p.q = (const uint8_t*)q;
+  p.k = (const uint8_t*)k;
+  p.v = (const uint8_t*)v;
+  p.dsq = descale_q;
+  p.dsk = descale_k;
+  p.dsv = descale_v;
+  p.out = (uint16_t*)out;
+  p.lse = lse;
+  p.kpm = key_padding_mask;
+  p.s_q = (int)s_q;
+  p.s_k = (int)s_k;
+  p.H = (int)H;
+  p.BH = (int)(B * H);
+  p.n_qt = (int)((s_q + 255) / 256);
+  p.scale = scale;
+  const int grid = p.BH * p.n_qt;
+  const bool pad = key_padding_mask != nullptr && s_k > 0;
+  const bool cz = causal != 0;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e;
+  if (d == 128) {
+    e = cz ? (pad ? launch<128, true, true>(p, grid, hs) : launch<128, true, false>(p, grid, hs))
+           : (pad ? launch<128, false, true>(p, grid, hs) : launch<128, false, false>(p, grid, hs));
+  } else {
+    e = cz ? (pad ? launch<64, true, true>(p, grid, hs) : launch<64, true, false>(p, grid, hs))
+           : (pad ? launch<64, false, true>(p, grid, hs) : launch<64, false, false>(p, grid, hs));
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_LAUNCH;
+  }
+  g_last_hip_error = 0;
+  return ATTN_OK;
+}

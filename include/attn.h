@@ -183,6 +183,50 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
  * sizes). Host-only. */
 int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t s_q);
 
+/*
+ * attn_fwd_fp8 - enqueue the attention forward pass over 8-bit floating-point
+ * inputs on `stream`.
+ *
+ * The news.hamidun.com glossary entry "Flash attention" (second paragraph)
+ * names FP8 precision as the method's third version's addition. The inputs
+ * are OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * largest finite magnitude 448, NaN = 0x7F / 0xFF), one code per byte; the
+ * real value of a code is descale[b*H + h] times its E4M3 value. The result
+ * is the attention operation of attn_fwd on those real values:
+ *
+ *     O[b,h,i,:] = sum_j softmax_j( scale * dq * dk * q8[b,h,i,:].k8[b,h,j,:] + mask ) dv * v8[b,h,j,:]
+ *
+ * with dq = descale_q[b*H + h] and so on. Both products run on the 8-bit
+ * matrix cores with float32 accumulation; the softmax weights, each at most
+ * 256 against a running reference max, are rounded to E4M3 (relative error
+ * at most 2^-4, or 2^-10 absolute below 2^-6) before the value product; the
+ * row max, row sums and the output accumulator are float32.
+ *
+ * Arguments: as attn_fwd, except
+ *   q, k, v    uint8 E4M3 codes [B, H, s, d], 16-byte aligned
+ *   descale_q, descale_k, descale_v
+ *              NULL (every factor 1) or device float32 [B*H], 4-byte
+ *              aligned, finite; any sign (a negative scale * dq * dk is
+ *              handled like a negative scale in attn_fwd)
+ *   out        bf16 [B, H, s_q, d]; lse float32 [B, H, s_q]:
+ *              lse = ln sum_j exp(scale * dq * dk * q8.k8_j) over visible keys
+ *
+ * Statuses, ownership and synchrony as attn_fwd (ATTN_ERR_ALIGN also covers
+ * the descale arrays, ATTN_ERR_ALIAS an out or lse overlapping them). Input
+ * codes 0x7F / 0xFF (NaN) give NaN results.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, const float* descale_q,
+                 const float* descale_k, const float* descale_v, void* out, float* lse,
+                 int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d, float scale,
+                 int causal, const uint8_t* key_padding_mask, void* stream);
+
+/* attn_fwd_fp8_validate - the host-side checks of attn_fwd_fp8 (same
+ * arguments, no stream); no launch, no HIP runtime call. */
+int attn_fwd_fp8_validate(const void* q, const void* k, const void* v, const float* descale_q,
+                          const float* descale_k, const float* descale_v, const void* out,
+                          const float* lse, int64_t B, int64_t H, int64_t s_q, int64_t s_k,
+                          int64_t d, float scale, int causal, const uint8_t* key_padding_mask);
+
 /* attn_status_str - a static, human-readable name for a status code. */
 const char* attn_status_str(int status);
 

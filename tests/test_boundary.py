@@ -34,9 +34,9 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert names == ["attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_split",
-                     "attn_fwd_split_workspace_bytes", "attn_fwd_validate", "attn_last_hip_error",
-                     "attn_status_str"]
+    assert names == ["attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_fp8",
+                     "attn_fwd_fp8_validate", "attn_fwd_split", "attn_fwd_split_workspace_bytes",
+                     "attn_fwd_validate", "attn_last_hip_error", "attn_status_str"]
     for n in names:
         assert hasattr(lib, n), n
     dyn = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
@@ -251,3 +251,52 @@ def test_bwd_empty_problems_are_no_ops(lib):
                 workspace=None)
     assert call_bwd(B=0, **null) == E.ATTN_OK
     assert call_bwd(s_q=0, s_k=0, **null) == E.ATTN_OK
+
+
+# attn_fwd_fp8: same fake addresses plus three descale arrays
+DSQ, DSK, DSV = (9 << 40), (10 << 40), (11 << 40)
+GOOD8 = dict(GOOD, dsq=DSQ, dsk=DSK, dsv=DSV)
+
+
+def call_fp8(fn, **over):
+    a = dict(GOOD8, **over)
+    args = [a[n] for n in ("q", "k", "v", "dsq", "dsk", "dsv", "out", "lse", "B", "H", "s_q",
+                           "s_k", "d", "scale", "causal", "key_padding_mask")]
+    if fn is E.attn_fwd_fp8:
+        return fn(*args, None)
+    return fn(*args)
+
+
+@pytest.mark.parametrize("fn", [E.attn_fwd_fp8_validate, E.attn_fwd_fp8], ids=["validate", "fwd"])
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), E.ATTN_ERR_NULL),
+    (dict(out=None), E.ATTN_ERR_NULL),
+    (dict(k=None), E.ATTN_ERR_NULL),
+    (dict(B=-1), E.ATTN_ERR_SHAPE),
+    (dict(s_k=(1 << 22) + 1), E.ATTN_ERR_SHAPE),
+    (dict(d=96), E.ATTN_ERR_HEAD_DIM),
+    (dict(q=Q + 8), E.ATTN_ERR_ALIGN),
+    (dict(v=V + 1), E.ATTN_ERR_ALIGN),
+    (dict(dsk=DSK + 2), E.ATTN_ERR_ALIGN),
+    (dict(out=K + 64), E.ATTN_ERR_ALIAS),
+    (dict(lse=DSV), E.ATTN_ERR_ALIAS),
+    (dict(out=DSQ - 16), E.ATTN_ERR_ALIAS),
+    (dict(scale=float("nan")), E.ATTN_ERR_SCALE),
+])
+def test_fp8_rejected_before_launch(lib, fn, over, code):
+    assert call_fp8(fn, **over) == code
+
+
+def test_fp8_valid_arguments_pass_validation(lib):
+    assert call_fp8(E.attn_fwd_fp8_validate) == E.ATTN_OK
+    assert call_fp8(E.attn_fwd_fp8_validate, dsq=None, dsk=None, dsv=None) == E.ATTN_OK
+    assert call_fp8(E.attn_fwd_fp8_validate, d=64, causal=0, key_padding_mask=None) == E.ATTN_OK
+    assert call_fp8(E.attn_fwd_fp8_validate, k=None, v=None, s_k=0) == E.ATTN_OK
+    # the inputs are one byte per element: an out placed right after q's bytes is fine
+    assert call_fp8(E.attn_fwd_fp8_validate, out=Q + 2 * 3 * 100 * 128) == E.ATTN_OK
+
+
+def test_fp8_empty_problems_are_no_ops(lib):
+    null = dict(q=None, k=None, v=None, out=None, lse=None, dsq=None, dsk=None, dsv=None)
+    assert call_fp8(E.attn_fwd_fp8, B=0, **null) == E.ATTN_OK
+    assert call_fp8(E.attn_fwd_fp8, s_q=0, **null) == E.ATTN_OK
