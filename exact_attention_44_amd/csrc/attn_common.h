@@ -51,7 +51,9 @@ __device__ __forceinline__ f32x16_t mfma_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) 
 // 480 up give NaN, so callers keep them below that), first value in the
 // lowest byte.
 __device__ __forceinline__ uint32_t pack_e4m3(float x0, float x1, float x2, float x3) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  // the first conversion keeps the upper half of its third operand, which the
+  // second one overwrites: any value will do, and x0's bits need no move
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __builtin_bit_cast(int, x0), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
   return (uint32_t)w;
 }

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   // Weights are taken against a reference max that can lag the true one;
   // their float32 tile sum bounds every weight, and E4M3 conversion turns
   // magnitudes from 480 up into NaN, so a tile whose sum exceeds 256 is
-  // recomputed against the true max.
+  // recomputed against the true max (see finish()).
   constexpr float kSumLimit = 256.f;
 
   __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF_BYTES];
@@ -236,7 +236,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t sc[KB];
-  i32x8_t pf;              // E4M3 weights of the tile between its two phases
+  float xw[KB][16];        // float32 weights of the tile between its two phases
+  i32x8_t pf;              // the same rounded to E4M3 (value product operand)
   uint32_t mbyte = 1u;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16_t{};
@@ -261,11 +262,30 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   constexpr int LA = 8;         // of them issued before the M step's barrier
   static_assert(LA <= N_VR, "prefetched reads must belong to the value product");
   i32x2_t vpre[LA];
-  // M step, first half: O^T += V_t^T P(t)^T.
-  auto pv = [&](int t) {
-    i32x2_t vr[N_VR];
+  // Operands of the two products: the value product's transpose reads (the
+  // first LA of them were issued before the M step's barrier) and the score
+  // product's K fragments.
+  i32x2_t vr[N_VR];
+  i32x8_t ka[KB][DK];
+  auto read_v = [&](int t) {
 #pragma unroll
     for (int i = 0; i < N_VR; ++i) vr[i] = i < LA ? vpre[i < LA ? i : 0] : v_read(t, i);
+  };
+  auto read_k = [&](int t) {
+    const char* kl = lds + (t % NBUF) * BUF_BYTES + k_lane_off;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4_t x = *(const u32x4_t*)(kl + kb * 32 * KS + kk * 64 + 16 * u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ka[kb][kk][4 * u + e] = (int)x[e];
+        }
+  };
+  // O^T += V_t^T P(t)^T.
+  auto pv_mfma = [&]() {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       i32x8_t a;
@@ -277,39 +297,92 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
       o[db] = mfma_e4m3(a, pf, o[db]);
     }
   };
-  // M step, second half: S(t)^T = K_t Q^T.
-  auto qk = [&](int t) {
-    const char* kl = lds + (t % NBUF) * BUF_BYTES + k_lane_off;
+  // S(t)^T = K_t Q^T (the key blocks' chains interleaved).
+  auto qk_mfma = [&](int t) {
+    f32x16_t acc[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      i32x8_t a[DK];
+    for (int kk = 0; kk < DK; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) {
+      for (int kb = 0; kb < KB; ++kb) acc[kb] = mfma_e4m3(ka[kb][kk], qf[kk], kk ? acc[kb] : f32x16_t{});
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4_t x = *(const u32x4_t*)(kl + kb * 32 * KS + kk * 64 + 16 * u);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a[kk][4 * u + e] = (int)x[e];
-        }
-      }
-      f32x16_t acc = {};
-#pragma unroll
-      for (int kk = 0; kk < DK; ++kk) acc = mfma_e4m3(a[kk], qf[kk], acc);
-      sc[kb] = acc;
-    }
+    for (int kb = 0; kb < KB; ++kb) sc[kb] = acc[kb];
     if (PADMASK) {
       const int key = t * BC + lane;
       mbyte = key < s_k ? (uint32_t)mg[key] : 1u;
     }
   };
+  auto qk = [&](int t) {
+    read_k(t);
+    qk_mfma(t);
+  };
+  // Weights of the scores in sc against the current reference max.
+  auto weights = [&](float nmc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xw[kb][r] = fmaf(sc[kb][r], c, nmc);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xw[kb][r] = __builtin_amdgcn_exp2f(xw[kb][r]);
+  };
+  auto row_sum = [&]() __attribute__((always_inline)) -> float {
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ps[r & 3] += xw[kb][r];
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+  // Start of an M step: the rest of the softmax of the tile whose scores are
+  // in sc (the V step before it took the exponentials). The tile's float32
+  // row sum bounds every weight; if it exceeds the limit (or overflowed) in
+  // any lane, the wave takes the true max, rescales O and l by
+  // exp2((m_old - m_new) c) and recomputes the weights (a lane whose row has
+  // no visible key yet keeps alpha = 1). Then the weights are rounded to E4M3
+  // as the value product's operand. This vector work sits in the M step
+  // because the V step, with the exponentials, is the longer of the two.
+  auto finish = [&]() __attribute__((always_inline)) {
+    float rs = row_sum();
+    if (__ballot(!(rs <= kSumLimit)) != 0ull) {
+      float mx = sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const bool none = m_new == -INFINITY;
+      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+      weights(none ? 0.f : -m_new * c);
+      rs = row_sum();
+    }
+    l_run += rs;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, r0 = 4 * (w & 3);
+      pf[w] = (int)pack_e4m3(xw[kb][r0], xw[kb][r0 + 1], xw[kb][r0 + 2], xw[kb][r0 + 3]);
+    }
+  };
+  // One M step: every LDS read first, then the softmax tail (its vector work
+  // covers the read latency), then the eight MFMAs.
   auto m_step = [&](int tp, int tq) {
     __builtin_amdgcn_s_setprio(2);
-    pv(tp);
-    qk(tq);
+    read_v(tp);
+    read_k(tq);
+    finish();
+    pv_mfma();
+    qk_mfma(tq);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
   };
-  // V step: staging of later tiles, then masks and online softmax of S(t).
+  // V step: staging of later tiles, then masks and the exponentials of S(t).
   auto vstep = [&](int t) {
     dma_k(t + 3);
     dma_v(t + 2);
@@ -345,50 +418,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (m_run == -INFINITY) m_run = mx;
     }
-    float nmc = -((m_run == -INFINITY) ? 0.f : m_run) * c;
-    auto weights = [&]() -> float {
-      float x[KB][16];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(sc[kb][r], c, nmc);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[kb][r] = __builtin_amdgcn_exp2f(x[kb][r]);
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ps[r & 3] += x[kb][r];
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int kb = w >> 2, r0 = 4 * (w & 3);
-        pf[w] = (int)pack_e4m3(x[kb][r0], x[kb][r0 + 1], x[kb][r0 + 2], x[kb][r0 + 3]);
-      }
-      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    };
-    float rs = weights();
-    if (__ballot(!(rs <= kSumLimit)) != 0ull) {
-      float mx = sc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const bool none = m_new == -INFINITY;
-      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-      nmc = none ? 0.f : -m_new * c;
-      rs = weights();
-    }
-    l_run += rs;
+    weights(-((m_run == -INFINITY) ? 0.f : m_run) * c);
   };
 
   if (n_kv > 0) {
@@ -437,7 +467,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     if (n_kv > 0) {
       vstep(n_kv - 1);
       vstep_sync(n_kv - 1);
-      pv(n_kv - 1);
+      read_v(n_kv - 1);
+      finish();
+      pv_mfma();
       phase_sync();
     }
     phase_sync();
@@ -455,7 +487,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
       vstep(t);
       vstep_sync(t);
     }
-    if (n_kv > 0) pv(n_kv - 1);
+    if (n_kv > 0) {
+      read_v(n_kv - 1);
+      finish();
+      pv_mfma();
+    }
     phase_sync();
   }
 
