@@ -29,13 +29,13 @@
 // from the row-major V tile with LDS transpose reads that gather, for each
 // lane's feature, the bytes of exactly those keys.
 //
-// LDS per tile: K row-major in key order, rows padded to D + 16 bytes (the 16
-// lanes of each 16-byte fragment read hit distinct banks). V row-major in
-// k-slot order: LDS row 32 h + j holds key(h, j), rows padded to D + 32
-// bytes, so each transpose read covers eight consecutive rows whose starts
-// fall in distinct 8-bank groups (conflict-free) and every read address is a
-// per-lane base plus compile-time offsets. Both tiles arrive by buffer loads
-// that write LDS directly.
+// LDS per tile: K row-major in key order, V row-major in k-slot order (LDS row
+// 32 h + j holds key(h, j), so each transpose read covers eight consecutive
+// rows), both with unpadded D-byte rows whose 16-byte slots are permuted by an
+// XOR with a function of the row (k_swz, v_swz) chosen so that every fragment
+// read hits distinct banks. Both tiles arrive by buffer loads that write LDS
+// directly; a half tile is a whole number of 64-slot load instructions, so
+// every wave issues the same loads.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -61,6 +61,23 @@ struct Fp8Params {
   float scale;
 };
 
+// XOR applied to the 16-byte slot index of K row r. A score-product fragment
+// read covers 16 consecutive rows at one logical slot; with D-byte rows the
+// bank group of (row, slot) is (r * D / 16 + slot) mod 16, and the XOR makes
+// the 16 rows' groups distinct.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+
+// XOR applied to the 16-byte slot index of V's LDS row r. A transpose read
+// covers eight consecutive rows at two adjacent slots per lane half; the XOR
+// (which keeps the low bit of the slot) makes their 16 bank groups distinct.
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? 2 * ((r >> 1) & 3) : 2 * ((r >> 2) & 1);
+}
+
 // Key (within the 64-key tile) at slot j of lane half h of the value
 // product's k axis: the key that score accumulator register j % 16 of key
 // block j / 16 holds in that lane half.
@@ -77,27 +94,17 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   constexpr int DK = D / 64;          // k-steps of the score product
   constexpr int DB = D / 32;          // 32-feature blocks of the output
   constexpr int KU = D / 16;          // 16-byte units per K or V row
-  constexpr int KS = D + 16;          // K row stride (bytes)
-  constexpr int VS = D + 32;          // V row stride (bytes)
-  constexpr int K_BYTES = BC * KS;
-  constexpr int V_BYTES = BC * VS;
+  constexpr int K_BYTES = BC * D;
+  constexpr int V_BYTES = BC * D;
   constexpr int BUF_BYTES = K_BYTES + V_BYTES;
   constexpr int NBUF = 4;
   // Each group stages half of a tile's LDS rows: K rows 32 grp .. +31 (keys
-  // 32 grp ..) and V rows 32 grp .. +31 (the keys of lane half grp). A half is
-  // 32 padded rows of 16-byte slots written by DMA instructions of 64
-  // consecutive slots each; the last instruction overlaps its predecessor
-  // (the overlap is written twice with the same data) and a padding slot
-  // receives a copy of its row's first 16 bytes.
-  constexpr int ROW_SLOTS = KS / 16;
-  constexpr int K_SLOTS = 32 * ROW_SLOTS;
-  constexpr int K_DMA = (K_SLOTS + 63) / 64;
-  constexpr int K_DMA_W = (K_DMA + 3) / 4;
-  constexpr int VROW_SLOTS = VS / 16;
-  constexpr int V_SLOTS = 32 * VROW_SLOTS;
-  constexpr int V_DMA = (V_SLOTS + 63) / 64;
-  constexpr int V_DMA_W = (V_DMA + 3) / 4;
-  static_assert(K_SLOTS >= 64 && V_SLOTS >= 64, "a half tile must fill one DMA instruction");
+  // 32 grp ..) and V rows 32 grp .. +31 (the keys of lane half grp), each
+  // 32 rows of KU 16-byte slots written by DMA instructions of 64 consecutive
+  // LDS slots; each lane loads the memory slot that belongs in its LDS slot.
+  constexpr int H_SLOTS = 32 * KU;
+  constexpr int N_DMA = H_SLOTS / 64;  // per half tile, of K and of V
+  static_assert(H_SLOTS % 64 == 0 && N_DMA <= 4, "a half tile is at most one DMA per wave");
   // Weights are taken against a reference max that can lag the true one;
   // their float32 tile sum bounds every weight, and E4M3 conversion turns
   // magnitudes from 480 up into NaN, so a tile whose sum exceeds 256 is
@@ -190,44 +197,26 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   }
 
   // ---- staging of this group's half (keys 32 grp .. 32 grp + 31) of a tile
-  const int wg = wv & 3;
-  uint32_t k_voff[K_DMA_W];
-#pragma unroll
-  for (int i = 0; i < K_DMA_W; ++i) {
-    const int j = wg + 4 * i;
-    const int slot = min(64 * j, K_SLOTS - 64) + lane;
-    const int row = 32 * grp + slot / ROW_SLOTS, un = slot % ROW_SLOTS;
-    k_voff[i] = (uint32_t)(row * D + (un < KU ? 16 * un : 0));
-  }
-  uint32_t v_voff[V_DMA_W];
-#pragma unroll
-  for (int i = 0; i < V_DMA_W; ++i) {
-    const int j = wg + 4 * i;
-    const int slot = min(64 * j, V_SLOTS - 64) + lane;
-    const int key = key_of_slot(grp, slot / VROW_SLOTS), un = slot % VROW_SLOTS;
-    v_voff[i] = (uint32_t)(key * D + (un < KU ? 16 * un : 0));
+  const int wg = wv & 3;  // this wave's DMA instruction within its group's half
+  uint32_t k_voff, v_voff;
+  {
+    const int slot = 64 * wg + lane;  // LDS slot within the half tile
+    const int r = slot / KU, ph = slot % KU;
+    k_voff = (uint32_t)((32 * grp + r) * D + 16 * (ph ^ k_swz<D>(r)));
+    v_voff = (uint32_t)(key_of_slot(grp, r) * D + 16 * (ph ^ v_swz<D>(r)));
   }
   auto dma_k = [&](int u) {
     const int j0 = u * BC;
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(kg + (int64_t)j0 * D, rest);
-    char* dst = lds + (u % NBUF) * BUF_BYTES + grp * K_SLOTS * 16;
-#pragma unroll
-    for (int i = 0; i < K_DMA_W; ++i) {
-      const int j = wg + 4 * i;
-      if (j < K_DMA) load16_to_lds(r, dst + min(64 * j, K_SLOTS - 64) * 16, k_voff[i]);
-    }
+    if (wg < N_DMA) load16_to_lds(r, lds + (u % NBUF) * BUF_BYTES + (grp * H_SLOTS + 64 * wg) * 16, k_voff);
   };
   auto dma_v = [&](int u) {
     const int j0 = u * BC;
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(vg + (int64_t)j0 * D, rest);
-    char* dst = lds + (u % NBUF) * BUF_BYTES + K_BYTES + grp * V_SLOTS * 16;
-#pragma unroll
-    for (int i = 0; i < V_DMA_W; ++i) {
-      const int j = wg + 4 * i;
-      if (j < V_DMA) load16_to_lds(r, dst + min(64 * j, V_SLOTS - 64) * 16, v_voff[i]);
-    }
+    if (wg < N_DMA)
+      load16_to_lds(r, lds + (u % NBUF) * BUF_BYTES + K_BYTES + (grp * H_SLOTS + 64 * wg) * 16, v_voff);
   };
 
   // ---- per-wave running state
@@ -242,20 +231,34 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16_t{};
 
-  const int k_lane_off = ln * KS + hl * 32;
-  // Transpose-read address of the value product's A operand. Lane L (group
+  // Score-product fragment reads: lane (ln, hl) reads K row 32 kb + ln at
+  // logical slot 4 kk + 2 hl + u (features 64 kk + 32 hl + 16 u ..); the
+  // swizzle depends on ln only (adding 32 rows leaves it unchanged).
+  int k_off[DK][2];
+#pragma unroll
+  for (int kk = 0; kk < DK; ++kk)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) k_off[kk][u] = ln * D + 16 * ((4 * kk + 2 * hl + u) ^ k_swz<D>(ln));
+  // Transpose-read addresses of the value product's A operand. Lane L (group
   // G = L / 16, x = L % 16, half h = G / 2) reads, for byte block tb and
   // feature block db, LDS row 32 h + 8 tb + x / 2 (key key(h, 8 tb + x / 2))
   // at features 32 db + 16 (G & 1) + 8 (x & 1) .. +7; the transpose hands
   // lane L the bytes of its own feature 32 db + L % 32 for the keys of slots
-  // 8 tb .. 8 tb + 7 of its half.
-  const int v_lane_off = (32 * (lane >> 5) + ((lane & 15) >> 1)) * VS + 16 * ((lane >> 4) & 1) +
-                         8 * (lane & 1);
+  // 8 tb .. 8 tb + 7 of its half. The row's swizzle does not depend on tb,
+  // and it keeps the slot's low bit, so the slot is 2 (db ^ s) + (G & 1).
+  int v_off[DB];
+  {
+    const int row = 32 * (lane >> 5) + ((lane & 15) >> 1);
+    const int sw = v_swz<D>(row) >> 1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      v_off[db] = row * D + 16 * (2 * (db ^ sw) + ((lane >> 4) & 1)) + 8 * (lane & 1);
+  }
   auto v_read = [&](int t, int i) -> i32x2_t {
     // read i of tile t's value product: feature block i / 4, byte block i % 4
-    const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + v_lane_off;
+    const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES;
     const int db = i >> 2, tb = i & 3;
-    return lds_read_tr8(vl + 8 * tb * VS + 32 * db);
+    return lds_read_tr8(vl + v_off[db] + 8 * tb * D);
   };
 
   constexpr int N_VR = 4 * DB;  // transpose reads per value product
@@ -272,14 +275,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     for (int i = 0; i < N_VR; ++i) vr[i] = i < LA ? vpre[i < LA ? i : 0] : v_read(t, i);
   };
   auto read_k = [&](int t) {
-    const char* kl = lds + (t % NBUF) * BUF_BYTES + k_lane_off;
+    const char* kl = lds + (t % NBUF) * BUF_BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int kk = 0; kk < DK; ++kk)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const u32x4_t x = *(const u32x4_t*)(kl + kb * 32 * KS + kk * 64 + 16 * u);
+          const u32x4_t x = *(const u32x4_t*)(kl + k_off[kk][u] + kb * 32 * D);
 #pragma unroll
           for (int e = 0; e < 4; ++e) ka[kb][kk][4 * u + e] = (int)x[e];
         }
