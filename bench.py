@@ -46,6 +46,7 @@ PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
 COPY_BYTES = 1 << 30
 KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_fwd.hip")
+KERNEL_SOURCE_FP8 = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_fwd_fp8.hip")
 
 # HBM bytes per launch from two rocprofv3 counter passes (FETCH_SIZE, then
 # WRITE_SIZE) of this script, each scaled by what the same counter reports for
@@ -56,6 +57,11 @@ MEASURED_TRAFFIC = {
         "source_sha256": "76d3b683251bc9eb7c6fb8f4100e6df415a46de4c057c96ea4acef7048e45143",
         "fetch_bytes": 492803164,
         "write_bytes": 68215136,
+    },
+    "fp8:B=1,H=32,s=8192,d=128,causal": {
+        "source_sha256": "566b89e677657e3de75130cf2cee5350189335a2d249883655d5d55655ee2680",
+        "fetch_bytes": 203621561,
+        "write_bytes": 68166424,
     },
 }
 
@@ -262,10 +268,11 @@ def main():
         algorithmic_bytes = 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d + 2 * w.B * w.H * w.s_q * w.d \
             + 4 * w.B * w.H * w.s_q
     traffic, traffic_detail = None, {"algorithmic_bytes": algorithmic_bytes}
-    measured = None if (a.backward or split or a.fp8) else MEASURED_TRAFFIC.get(w.name)
+    measured = None if (a.backward or split) else \
+        MEASURED_TRAFFIC.get(("fp8:" if a.fp8 else "") + w.name)
     if measured is not None:
         import hashlib
-        with open(KERNEL_SOURCE, "rb") as f:
+        with open(KERNEL_SOURCE_FP8 if a.fp8 else KERNEL_SOURCE, "rb") as f:
             current = hashlib.sha256(f.read()).hexdigest()
         if current == measured["source_sha256"]:
             traffic = measured["fetch_bytes"] + measured["write_bytes"]
