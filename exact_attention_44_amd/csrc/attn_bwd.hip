@@ -22,9 +22,12 @@
 //               dV^T += dO^T P and dK^T += Q^T dS.
 // In both, the rows of the LDS operand are read in the permuted order of
 // key_of_row, so the 32x32 accumulators are the bf16 operands of the next
-// product after a conversion, with no shuffles. LDS tiles are stored both
-// row-major (operands of the score-like products) and transposed (operands of
-// the gradient products), the transpose done in registers while storing.
+// product after a conversion, with no shuffles. The dq kernel stages its K tile
+// both row-major and transposed (the transpose done in registers while
+// storing). The dkv kernel loads its Q and dO tiles straight into LDS,
+// row-major, and reads the transposed operands of the gradient products with
+// LDS transpose reads; it also loads the rows' lse*log2(e) and D, which the dq
+// kernel writes to the workspace.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -48,9 +51,11 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;        // D = rowsum(dO * O), float32 [B*H][s_q] (workspace)
+  float* delta;        // D = rowsum(dO * O), float32 [B*H][s_qp] (workspace)
+  float* lse2w;        // lse * log2(e), -inf for empty or padding rows, [B*H][s_qp]
   const uint8_t* kpm;
   int s_q, s_k, H, BH, n_qt, n_kt;
+  int s_qp;            // s_q rounded up to 64: workspace rows per (b, h)
   float c;             // scale * log2(e): weights are exp2(q.k c - lse log2(e))
   float scale;
 };
@@ -193,7 +198,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
   const float lse_row = row < s_q ? p.lse[(int64_t)bh * s_q + row] : -INFINITY;
   const bool live = lse_row != -INFINITY;  // a row with no visible key has P = 0
   const float lse2 = live ? lse_row * kLog2e : 0.f;
-  if (hl == 0 && row < s_q) p.delta[(int64_t)bh * s_q + row] = Dv;
+  // D and lse*log2(e) for the dkv kernel, which loads them 64 rows at a time:
+  // the rows up to the next multiple of 64 are written too (D = 0, lse = -inf,
+  // so they carry no weight)
+  if (hl == 0 && row < p.s_qp) {
+    const int64_t wi = (int64_t)bh * p.s_qp + row;
+    p.delta[wi] = row < s_q ? Dv : 0.f;
+    p.lse2w[wi] = (row < s_q && live) ? lse2 : -INFINITY;
+  }
 
   Stager<D, BC, NI> sk, sv;
   auto load_tile = [&](int u) {
@@ -310,13 +322,35 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dkv kernel
 // ---------------------------------------------------------------------------
+// XOR applied to the 16-byte slot index of row r of a bf16 Q or dO tile in LDS
+// (unpadded rows of 2D bytes; it depends on r mod 16 only). The score-side
+// reads take one slot of 16 rows (a permutation of an aligned group of 16);
+// the transpose reads take 4 adjacent slots of 4 adjacent rows per half wave;
+// with this permutation both kinds of read hit distinct banks.
+template <int D>
+__device__ __forceinline__ int q_swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 2) << 1) | ((r >> 2) & 3));
+}
+
+// 16-bit LDS transpose read: within each group of 16 lanes, element k (0..3)
+// of lane i = 4j + c comes from the address given by lane 4k + j of the
+// group, plus c elements.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const char* p) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p));
+}
+
 template <int D, bool CAUSAL, bool PADMASK>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdParams p) {
   constexpr int NT = 256, BK = 128, BQ = 64;
   constexpr int QB = BQ / 32, DK = D / 16, DB = D / 32;
-  using QTl = Tile<D, BQ>;                // Q and dO: row-major and transposed
-  constexpr int BUF = 2 * QTl::BYTES + 2 * BQ * 4;  // Q, dO, lse*log2e, D
-  constexpr int NI = (QTl::ITEMS + NT - 1) / NT;
+  constexpr int RB = 2 * D;                   // bytes per Q / dO row in LDS
+  constexpr int SL = D / 8;                   // 16-byte slots per row
+  constexpr int TILE = BQ * RB;               // one Q or dO tile
+  constexpr int BUF = 2 * TILE + 2 * BQ * 4;  // Q, dO, lse*log2e, D
+  constexpr int NQ = BQ * SL / NT;            // loads per wave per Q or dO tile
+  static_assert((BQ * SL) % NT == 0, "a tile is a whole number of loads per wave");
 
   __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
@@ -350,31 +384,34 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdParams p) {
   const int qt1 = (s_q + BQ - 1) / BQ;
   const uint16_t* qg = p.q + (int64_t)bh * s_q * D;
   const uint16_t* dg = p.dout + (int64_t)bh * s_q * D;
-  const float* lg = p.lse + (int64_t)bh * s_q;
-  const float* Dg = p.delta + (int64_t)bh * s_q;
+  const float* l2g = p.lse2w + (int64_t)bh * p.s_qp;
+  const float* Dg = p.delta + (int64_t)bh * p.s_qp;
 
-  Stager<D, BQ, NI> sq, sd;
-  float st_l = 0.f, st_d = 0.f;
-  auto load_tile = [&](int u) {
+  // Staging: loads that write LDS directly. Load i of this wave fills LDS
+  // slots 64 (4 i + wv) .. +63 of the Q and of the dO tile; each lane loads
+  // the memory slot that belongs in its LDS slot. Rows past s_q read zeros.
+  uint32_t q_voff[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int sl = 64 * (4 * i + wv) + lane;
+    const int r = sl / SL, ph = sl % SL;
+    q_voff[i] = (uint32_t)(r * RB + 16 * (ph ^ q_swz<D>(r)));
+  }
+  auto dma_tile = [&](int u, int bi) {
     const int i0 = u * BQ;
-    sq.load(qg + (int64_t)i0 * D, s_q - i0, tid, NT);
-    sd.load(dg + (int64_t)i0 * D, s_q - i0, tid, NT);
-    if (tid < BQ) {
-      const int i = i0 + tid;
-      const float l = i < s_q ? lg[i] : -INFINITY;
-      st_l = l;  // -inf marks a row with no visible key (or past s_q)
-      st_d = i < s_q ? Dg[i] : 0.f;
-    }
-  };
-  auto store_tile = [&](int u) {
-    char* base = lds + (u & 1) * BUF;
-    sq.store(base, tid, NT);
-    sd.store(base + QTl::BYTES, tid, NT);
-    if (tid < BQ) {
-      float* lw = (float*)(base + 2 * QTl::BYTES);
-      lw[tid] = st_l == -INFINITY ? -INFINITY : st_l * kLog2e;
-      lw[BQ + tid] = st_d;
-    }
+    char* base = lds + bi * BUF;
+    const uint32_t rest = (uint32_t)max(s_q - i0, 0) * RB;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + (int64_t)i0 * D, rest);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dg + (int64_t)i0 * D, rest);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) load16_to_lds(rq, base + 64 * (4 * i + wv) * 16, q_voff[i]);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) load16_to_lds(rd, base + TILE + 64 * (4 * i + wv) * 16, q_voff[i]);
+    // lse*log2e then D of the tile's 64 rows, 16 slots each: wave wv loads
+    // slots 8 (wv & 1) .. +7 of lse*log2e (waves 0, 1) or of D (waves 2, 3).
+    // The workspace holds s_qp >= i0 + 64 rows per (b, h).
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc((wv < 2 ? l2g : Dg) + i0, BQ * 4);
+    if (lane < 8) load16_to_lds(rl, base + 2 * TILE + 128 * wv, (uint32_t)(16 * (8 * (wv & 1) + lane)));
   };
 
   f32x16_t dkt[DB], dvt[DB];
@@ -383,23 +420,44 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdParams p) {
     dkt[db] = f32x16_t{};
     dvt[db] = f32x16_t{};
   }
-  const int a_off = key_of_row(ln) * QTl::RS + hl * 16;
-  const int t_off = ln * QTl::TS + hl * 16;
+  // Score-side fragment reads: lane (ln, hl) reads row key_of_row(ln) of each
+  // 32-row block at logical slot 2 kk + hl (features 16 kk + 8 hl ..).
+  int a_off[DK];
+  {
+    const int r = key_of_row(ln);
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) a_off[kk] = r * RB + 16 * ((2 * kk + hl) ^ q_swz<D>(r));
+  }
+  // Transpose reads of the gradient products' A operands (Q^T, dO^T: rows =
+  // features, k = 16 queries of a k-step). Lane a of 16-lane group G (half
+  // hl = G / 2, g = G & 1) gives, for read r of feature block db, the address
+  // of query row 8 hl + 4 r + a / 4 of the k-step at features
+  // 32 db + 16 g + 4 (a & 3) .. +3; lane L then holds feature 32 db + L % 32 of
+  // queries 8 hl + 4 r .. +3, elements 4 r .. 4 r + 3 of its operand.
+  int t_off[2][DB];
+  {
+    const int a = lane & 15, g = (lane >> 4) & 1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = 8 * hl + 4 * r + (a >> 2);
+        const int slot = 4 * db + 2 * g + ((a & 3) >> 1);
+        t_off[r][db] = row * RB + 16 * (slot ^ q_swz<D>(row)) + 8 * (a & 1);
+      }
+  }
   const int n_it = qt1 - qt0;
 
-  if (n_it > 0) {
-    load_tile(qt0);
-    store_tile(qt0);
-  }
+  if (n_it > 0) dma_tile(qt0, 0);
   __syncthreads();
   for (int it = 0; it < n_it; ++it) {
     const int u = qt0 + it;
-    if (it + 1 < n_it) load_tile(u + 1);
-    const char* ql = lds + (u & 1) * BUF;
-    const char* qtl = ql + QTl::ROW_BYTES;
-    const char* dl = ql + QTl::BYTES;
-    const char* dtl = dl + QTl::ROW_BYTES;
-    const float* lw = (const float*)(ql + 2 * QTl::BYTES);
+    // the other buffer was last read in the previous iteration, before its
+    // closing barrier; this barrier's wait also covers the new loads
+    if (it + 1 < n_it) dma_tile(u + 1, (it + 1) & 1);
+    const char* ql = lds + (it & 1) * BUF;
+    const char* dl = ql + TILE;
+    const float* lw = (const float*)(ql + 2 * TILE);
     const int i0 = u * BQ;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -408,8 +466,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdParams p) {
       f32x16_t s = {}, dp = {};
 #pragma unroll
       for (int kk = 0; kk < DK; ++kk) {
-        const bf16x8_t fq = *(const bf16x8_t*)(ql + a_off + qb * 32 * QTl::RS + kk * 32);
-        const bf16x8_t fd = *(const bf16x8_t*)(dl + a_off + qb * 32 * QTl::RS + kk * 32);
+        const bf16x8_t fq = *(const bf16x8_t*)(ql + a_off[kk] + qb * 32 * RB);
+        const bf16x8_t fd = *(const bf16x8_t*)(dl + a_off[kk] + qb * 32 * RB);
         s = mfma(fq, kf[kk], s);
         dp = mfma(fd, vf[kk], dp);
       }
@@ -447,17 +505,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdParams p) {
         pp[ks] = __builtin_bit_cast(bf16x8_t, w1);
         pd[ks] = __builtin_bit_cast(bf16x8_t, w2);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (A: transposed tiles; B: this lane's key)
+      // dV^T += dO^T P and dK^T += Q^T dS (A: transpose reads; B: this lane's key)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int off = t_off + db * 32 * QTl::TS + (4 * qb + 2 * ks) * 16;
-          dvt[db] = mfma(*(const bf16x8_t*)(dtl + off), pp[ks], dvt[db]);
-          dkt[db] = mfma(*(const bf16x8_t*)(qtl + off), pd[ks], dkt[db]);
+          const int o0 = t_off[0][db] + (32 * qb + 16 * ks) * RB;
+          const int o1 = t_off[1][db] + (32 * qb + 16 * ks) * RB;
+          const u32x2_t d0 = lds_read_tr16(dl + o0), d1 = lds_read_tr16(dl + o1);
+          const u32x2_t q0 = lds_read_tr16(ql + o0), q1 = lds_read_tr16(ql + o1);
+          const u32x4_t ad = {d0[0], d0[1], d1[0], d1[1]};
+          const u32x4_t aq = {q0[0], q0[1], q1[0], q1[1]};
+          dvt[db] = mfma(__builtin_bit_cast(bf16x8_t, ad), pp[ks], dvt[db]);
+          dkt[db] = mfma(__builtin_bit_cast(bf16x8_t, aq), pd[ks], dkt[db]);
         }
     }
-    if (it + 1 < n_it) store_tile(u + 1);
     __syncthreads();
   }
 
@@ -510,9 +572,13 @@ bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 
 }  // namespace
 
+// Rows of the workspace per (b, h): s_q rounded up to the dkv kernel's 64-row
+// query tiles.
+static int64_t ws_rows(int64_t s_q) { return (s_q + 63) / 64 * 64; }
+
 extern "C" int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t s_q) {
   if (B < 0 || H < 0 || s_q < 0) return -1;
-  return (B * H * s_q * 4 + 255) / 256 * 256;
+  return (2 * B * H * ws_rows(s_q) * 4 + 255) / 256 * 256;
 }
 
 extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -568,7 +634,9 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.dq = (uint16_t*)dq;
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;
+  p.s_qp = (int)ws_rows(s_q);
   p.delta = (float*)workspace;
+  p.lse2w = (float*)workspace + BH * p.s_qp;
   p.kpm = key_padding_mask;
   p.s_q = (int)s_q;
   p.s_k = (int)s_k;

@@ -159,8 +159,9 @@ int64_t attn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t s_q, int64_
  *   dk, dv bf16 [B, H, s_k, d]  written (zero for keys no query sees)
  *   workspace        caller-owned device memory, 256-byte aligned, of at
  *                    least attn_bwd_workspace_bytes(B, H, s_q) bytes (it
- *                    holds D, float32 [B, H, s_q]); contents on entry are
- *                    ignored and on return unspecified
+ *                    holds D = rowsum(dO * O) and lse * log2(e), float32,
+ *                    each [B, H, s_q rounded up to 64]); contents on entry
+ *                    are ignored and on return unspecified
  *   workspace_bytes  its size
  *   stream           a hipStream_t (NULL = the default stream)
  *
@@ -179,7 +180,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              float scale, int causal, const uint8_t* key_padding_mask,
              void* workspace, int64_t workspace_bytes, void* stream);
 
-/* attn_bwd_workspace_bytes - workspace bytes attn_bwd needs (-1 for negative
+/* attn_bwd_workspace_bytes - workspace bytes attn_bwd needs:
+ * 2 * B * H * (s_q rounded up to 64) * 4, rounded up to 256 (-1 for negative
  * sizes). Host-only. */
 int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t s_q);
 

@@ -208,7 +208,7 @@ def test_split_empty_problems_are_no_ops(lib):
 DO, DQ, DK, DV, BWS = (8 << 40), (9 << 40), (10 << 40), (11 << 40), (12 << 40)
 BGOOD = dict(q=Q, k=K, v=V, out=OUT, dout=DO, lse=LSE, dq=DQ, dk=DK, dv=DV, B=2, H=3, s_q=100,
              s_k=90, d=128, scale=0.1, causal=1, key_padding_mask=KPM, workspace=BWS,
-             workspace_bytes=2 * 3 * 100 * 4 + 256)
+             workspace_bytes=2 * 2 * 3 * 128 * 4)
 
 
 def call_bwd(**over):
@@ -219,8 +219,10 @@ def call_bwd(**over):
 
 
 def test_bwd_workspace_bytes(lib):
-    assert E.attn_bwd_workspace_bytes(2, 3, 100) == 2560
-    assert E.attn_bwd_workspace_bytes(1, 32, 8192) == 32 * 8192 * 4
+    # two float32 arrays (D and lse*log2e) of s_q rounded up to 64 rows per (b, h)
+    assert E.attn_bwd_workspace_bytes(2, 3, 100) == 2 * 6 * 128 * 4
+    assert E.attn_bwd_workspace_bytes(1, 32, 8192) == 2 * 32 * 8192 * 4
+    assert E.attn_bwd_workspace_bytes(1, 1, 1) == 512
     assert E.attn_bwd_workspace_bytes(-1, 3, 100) == -1
 
 
