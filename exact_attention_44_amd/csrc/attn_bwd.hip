@@ -22,12 +22,11 @@
 //               dV^T += dO^T P and dK^T += Q^T dS.
 // In both, the rows of the LDS operand are read in the permuted order of
 // key_of_row, so the 32x32 accumulators are the bf16 operands of the next
-// product after a conversion, with no shuffles. The dq kernel stages its K tile
-// both row-major and transposed (the transpose done in registers while
-// storing). The dkv kernel loads its Q and dO tiles straight into LDS,
-// row-major, and reads the transposed operands of the gradient products with
-// LDS transpose reads; it also loads the rows' lse*log2(e) and D, which the dq
-// kernel writes to the workspace.
+// product after a conversion, with no shuffles. The tiles that walk (K and V
+// in the dq kernel, Q and dO in the dkv kernel) are loaded straight into LDS,
+// row-major, and the transposed operands of the gradient products are read
+// with LDS transpose reads. The dkv kernel also loads the rows' lse*log2(e)
+// and D, which the dq kernel writes to the workspace.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -60,59 +59,25 @@ struct BwdParams {
   float scale;
 };
 
-// LDS tile of BT rows x D columns, stored row-major (row stride 2D+16 bytes)
-// and transposed (row stride 2BT+16 bytes). With these strides every 16-lane
-// fragment read hits distinct banks and each lane's fragment addresses are a
-// base plus immediate offsets.
-template <int D, int BT>
-struct Tile {
-  static constexpr int RS = 2 * D + 16;        // row-major stride
-  static constexpr int TS = 2 * BT + 16;       // transposed stride
-  static constexpr int ROW_BYTES = BT * RS;
-  static constexpr int T_BYTES = D * TS;
-  static constexpr int BYTES = ROW_BYTES + T_BYTES;
-  // items of 2 rows x 8 columns: loaded as two 16-byte pieces, stored as two
-  // row-major pieces and 8 transposed dwords
-  static constexpr int ITEMS = (BT / 2) * (D / 8);
-};
+// XOR applied to the 16-byte slot index of row r of a 64-row bf16 tile in LDS
+// (K and V in the dq kernel, Q and dO in the dkv kernel; unpadded rows of 2D
+// bytes; it depends on r mod 16 only). The score-side
+// reads take one slot of 16 rows (a permutation of an aligned group of 16);
+// the transpose reads take 4 adjacent slots of 4 adjacent rows per half wave;
+// with this permutation both kinds of read hit distinct banks.
+template <int D>
+__device__ __forceinline__ int q_swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 2) << 1) | ((r >> 2) & 3));
+}
 
-// Stage items [first, first + n*stride) of one BT x D tile: rows beyond
-// `rows` (and all of a tile past the end) read zeros through the range check.
-template <int D, int BT, int N>
-struct Stager {
-  u32x4_t r[N][2];
-  __device__ __forceinline__ void load(const uint16_t* base, int rows, int first, int stride) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)max(rows, 0) * D * 2);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int id = first + i * stride;
-      if (id < Tile<D, BT>::ITEMS) {
-        const int rp = id % (BT / 2), dc = id / (BT / 2);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) r[i][e] = load16(rs, (uint32_t)((2 * rp + e) * D + 8 * dc) * 2);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* tile, int first, int stride) const {
-    using T = Tile<D, BT>;
-    char* tt = tile + T::ROW_BYTES;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int id = first + i * stride;
-      if (id < T::ITEMS) {
-        const int rp = id % (BT / 2), dc = id / (BT / 2);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) *(u32x4_t*)(tile + (2 * rp + e) * T::RS + dc * 16) = r[i][e];
-        char* dst = tt + (8 * dc) * T::TS + (2 * rp) * 2;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-          *(uint32_t*)(dst + c * T::TS) = __builtin_amdgcn_perm(r[i][1][c >> 1], r[i][0][c >> 1], sel);
-        }
-      }
-    }
-  }
-};
+// 16-bit LDS transpose read: within each group of 16 lanes, element k (0..3)
+// of lane i = 4j + c comes from the address given by lane 4k + j of the
+// group, plus c elements.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const char* p) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p));
+}
 
 // Last unpadded key + 1 of batch item b (0 if all are padded); every thread
 // of the workgroup gets the value.
@@ -150,10 +115,12 @@ template <int D, bool CAUSAL, bool PADMASK>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int NT = 256, BR = 128, BC = 64;
   constexpr int KB = BC / 32, DK = D / 16, DB = D / 32;
-  using KT = Tile<D, BC>;                 // K: row-major and transposed
-  constexpr int VRS = 2 * D + 16;         // V: row-major only
-  constexpr int BUF = KT::BYTES + BC * VRS;
-  constexpr int NI = (KT::ITEMS + NT - 1) / NT;  // items per thread
+  constexpr int RB = 2 * D;               // bytes per K / V row in LDS
+  constexpr int SL = D / 8;               // 16-byte slots per row
+  constexpr int TILE = BC * RB;           // one K or V tile
+  constexpr int BUF = 2 * TILE;
+  constexpr int NQ = BC * SL / NT;        // loads per wave per K or V tile
+  static_assert((BC * SL) % NT == 0, "a tile is a whole number of loads per wave");
 
   __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
   __shared__ int lds_last;
@@ -207,44 +174,61 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
     p.lse2w[wi] = (row < s_q && live) ? lse2 : -INFINITY;
   }
 
-  Stager<D, BC, NI> sk, sv;
-  auto load_tile = [&](int u) {
+  // Staging: loads that write LDS directly (as in the dkv kernel). Load i of
+  // this wave fills LDS slots 64 (4 i + wv) .. +63 of the K and of the V tile.
+  // Keys past s_k read zeros.
+  uint32_t k_voff[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int sl = 64 * (4 * i + wv) + lane;
+    const int r = sl / SL, ph = sl % SL;
+    k_voff[i] = (uint32_t)(r * RB + 16 * (ph ^ q_swz<D>(r)));
+  }
+  auto dma_tile = [&](int u, int bi) {
     const int j0 = u * BC;
-    sk.load(kg + (int64_t)j0 * D, s_k - j0, tid, NT);
-    sv.load(vg + (int64_t)j0 * D, s_k - j0, tid, NT);
-  };
-  auto store_tile = [&](int u) {
-    char* base = lds + (u & 1) * BUF;
-    sk.store(base, tid, NT);
-    // V row-major only
-    char* vl = base + KT::BYTES;
+    char* base = lds + bi * BUF;
+    const uint32_t rest = (uint32_t)max(s_k - j0, 0) * RB;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (int64_t)j0 * D, rest);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (int64_t)j0 * D, rest);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int id = tid + i * NT;
-      if (id < KT::ITEMS) {
-        const int rp = id % (BC / 2), dc = id / (BC / 2);
+    for (int i = 0; i < NQ; ++i) load16_to_lds(rk, base + 64 * (4 * i + wv) * 16, k_voff[i]);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) *(u32x4_t*)(vl + (2 * rp + e) * VRS + dc * 16) = sv.r[i][e];
-      }
-    }
+    for (int i = 0; i < NQ; ++i) load16_to_lds(rv, base + TILE + 64 * (4 * i + wv) * 16, k_voff[i]);
   };
 
   f32x16_t dqt[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqt[db] = f32x16_t{};
-  const int a_off = key_of_row(ln) * KT::RS + hl * 16;  // row-major fragment base
-  const int t_off = ln * KT::TS + hl * 16;              // transposed fragment base
-
-  if (n_kv > 0) {
-    load_tile(0);
-    store_tile(0);
+  // score-side fragment offsets (row key_of_row(ln) of each 32-row block,
+  // logical slot 2 kk + hl) and transpose-read offsets of K^T (see the dkv
+  // kernel, which reads its Q^T and dO^T the same way)
+  int a_off[DK];
+  {
+    const int r = key_of_row(ln);
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) a_off[kk] = r * RB + 16 * ((2 * kk + hl) ^ q_swz<D>(r));
   }
+  int t_off[2][DB];
+  {
+    const int a = lane & 15, g = (lane >> 4) & 1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int rw = 8 * hl + 4 * r + (a >> 2);
+        const int slot = 4 * db + 2 * g + ((a & 3) >> 1);
+        t_off[r][db] = rw * RB + 16 * (slot ^ q_swz<D>(rw)) + 8 * (a & 1);
+      }
+  }
+
+  if (n_kv > 0) dma_tile(0, 0);
   __syncthreads();
   for (int t = 0; t < n_kv; ++t) {
-    if (t + 1 < n_kv) load_tile(t + 1);
+    // the other buffer was last read in the previous iteration, before its
+    // closing barrier; this barrier's wait also covers the new loads
+    if (t + 1 < n_kv) dma_tile(t + 1, (t + 1) & 1);
     const char* kl = lds + (t & 1) * BUF;
-    const char* ktl = kl + KT::ROW_BYTES;
-    const char* vl = kl + KT::BYTES;
+    const char* vl = kl + TILE;
     const int j0 = t * BC;
     // S^T = K Q^T and dP^T = V dO^T, one 32-key block at a time
     f32x16_t sc[KB], dp[KB];
@@ -253,8 +237,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
       f32x16_t a1 = {}, a2 = {};
 #pragma unroll
       for (int kk = 0; kk < DK; ++kk) {
-        const bf16x8_t fk = *(const bf16x8_t*)(kl + a_off + kb * 32 * KT::RS + kk * 32);
-        const bf16x8_t fv = *(const bf16x8_t*)(vl + key_of_row(ln) * VRS + hl * 16 + kb * 32 * VRS + kk * 32);
+        const bf16x8_t fk = *(const bf16x8_t*)(kl + a_off[kk] + kb * 32 * RB);
+        const bf16x8_t fv = *(const bf16x8_t*)(vl + a_off[kk] + kb * 32 * RB);
         a1 = mfma(fk, qf[kk], a1);
         a2 = mfma(fv, df[kk], a2);
       }
@@ -291,17 +275,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
         pf[kb][ks] = __builtin_bit_cast(bf16x8_t, w);
       }
     }
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T (A: transpose reads of the key tile)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8_t a = *(const bf16x8_t*)(ktl + t_off + db * 32 * KT::TS + (4 * kb + 2 * ks) * 16);
-          dqt[db] = mfma(a, pf[kb][ks], dqt[db]);
+          const u32x2_t k0v = lds_read_tr16(kl + t_off[0][db] + (32 * kb + 16 * ks) * RB);
+          const u32x2_t k1v = lds_read_tr16(kl + t_off[1][db] + (32 * kb + 16 * ks) * RB);
+          const u32x4_t a = {k0v[0], k0v[1], k1v[0], k1v[1]};
+          dqt[db] = mfma(__builtin_bit_cast(bf16x8_t, a), pf[kb][ks], dqt[db]);
         }
-    if (t + 1 < n_kv) store_tile(t + 1);
     __syncthreads();
   }
 
@@ -322,25 +307,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dkv kernel
 // ---------------------------------------------------------------------------
-// XOR applied to the 16-byte slot index of row r of a bf16 Q or dO tile in LDS
-// (unpadded rows of 2D bytes; it depends on r mod 16 only). The score-side
-// reads take one slot of 16 rows (a permutation of an aligned group of 16);
-// the transpose reads take 4 adjacent slots of 4 adjacent rows per half wave;
-// with this permutation both kinds of read hit distinct banks.
-template <int D>
-__device__ __forceinline__ int q_swz(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 2) << 1) | ((r >> 2) & 3));
-}
-
-// 16-bit LDS transpose read: within each group of 16 lanes, element k (0..3)
-// of lane i = 4j + c comes from the address given by lane 4k + j of the
-// group, plus c elements.
-__device__ __forceinline__ u32x2_t lds_read_tr16(const char* p) {
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-  return __builtin_bit_cast(
-      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p));
-}
-
 template <int D, bool CAUSAL, bool PADMASK>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdParams p) {
   constexpr int NT = 256, BK = 128, BQ = 64;
