@@ -112,7 +112,7 @@ __device__ int keys_until_last_unpadded(const uint8_t* mg, int s_k, int* lds_las
 // dq kernel
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool PADMASK>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int NT = 256, BR = 128, BC = 64;
   constexpr int KB = BC / 32, DK = D / 16, DB = D / 32;
   constexpr int RB = 2 * D;               // bytes per K / V row in LDS
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
 // dkv kernel
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool PADMASK>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdParams p) {
   constexpr int NT = 256, BK = 128, BQ = 64;
   constexpr int QB = BQ / 32, DK = D / 16, DB = D / 32;
   constexpr int RB = 2 * D;                   // bytes per Q / dO row in LDS
