@@ -112,8 +112,11 @@ __device__ int keys_until_last_unpadded(const uint8_t* mg, int s_k, int* lds_las
 // dq kernel
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool PADMASK>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dq_kernel(BwdParams p) {
-  constexpr int NT = 256, BR = 128, BC = 64;
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
+  // 32-key tiles at d = 128 keep the kernel within 256 registers, so two
+  // workgroups share a CU and one's staging and softmax overlap the other's
+  // matrix work
+  constexpr int NT = 256, BR = 128, BC = D == 128 ? 32 : 64;
   constexpr int KB = BC / 32, DK = D / 16, DB = D / 32;
   constexpr int RB = 2 * D;               // bytes per K / V row in LDS
   constexpr int SL = D / 8;               // 16-byte slots per row
