@@ -266,8 +266,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ko = 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
-        const bool hide = !live || ((sh >> (16 * (r >> 3) + (r & 7))) & 1u) || (CAUSAL && ko > lim);
-        const float pw = hide ? 0.f : __builtin_amdgcn_exp2f(fmaf(sc[kb][r], p.c, -lse2));
+        const bool hide = !live | (((sh >> (16 * (r >> 3) + (r & 7))) & 1u) != 0u) | (CAUSAL && ko > lim);
+        const float pw = __builtin_amdgcn_exp2f(hide ? -INFINITY : fmaf(sc[kb][r], p.c, -lse2));
         ds[r] = pw * (dp[kb][r] - Dv);
       }
 #pragma unroll
@@ -347,6 +347,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdP
   }
   bool kvis = key < s_k;
   if (PADMASK && kvis) kvis = p.kpm[(int64_t)b * s_k + key] == 0;
+  // causal: this key is hidden from query qi when kcut > qi (every query
+  // when the key itself is hidden)
+  const int kcut = kvis ? key : INT_MAX;
 
   // query tiles that can see a key of this tile
   const int qt0 = CAUSAL ? min(k0, s_q) / BQ : 0;
@@ -430,6 +433,22 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdP
     const int i0 = u * BQ;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      // Three scheduling regions per 32-query block. One wave per SIMD hides
+      // LDS latency only by issuing reads ahead of their use:
+      // (1) the score-side fragments, LA reads ahead of the 16 score MFMAs;
+      // (2) the 32 transpose reads of the gradient operands, then the vector
+      //     work (P, dS) that covers their latency;
+      // (3) the 16 gradient MFMAs.
+      constexpr int LA = 6;
+      f32x4_t lv[4], dv4[4];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int qo = 32 * qb + 16 * h2 + 8 * hl;
+        lv[2 * h2] = *(const f32x4_t*)(lw + qo);
+        lv[2 * h2 + 1] = *(const f32x4_t*)(lw + qo + 4);
+        dv4[2 * h2] = *(const f32x4_t*)(lw + BQ + qo);
+        dv4[2 * h2 + 1] = *(const f32x4_t*)(lw + BQ + qo + 4);
+      }
       // S = Q K^T and dP = dO V^T for 32 queries: one key per lane, the
       // registers hold queries 32qb + {8h..8h+7, 16+8h..16+8h+7}
       f32x16_t s = {}, dp = {};
@@ -440,26 +459,42 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdP
         s = mfma(fq, kf[kk], s);
         dp = mfma(fd, vf[kk], dp);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8 + LA, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * DK - LA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      u32x2_t tq[2][DB][2], td[2][DB][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int o = t_off[r][db] + (32 * qb + 16 * ks) * RB;
+            td[ks][db][r] = lds_read_tr16(dl + o);
+            tq[ks][db][r] = lds_read_tr16(ql + o);
+          }
       float lr[16], dr[16];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int qo = 32 * qb + 16 * h2 + 8 * hl;
-        const f32x4_t l0 = *(const f32x4_t*)(lw + qo), l1 = *(const f32x4_t*)(lw + qo + 4);
-        const f32x4_t d0 = *(const f32x4_t*)(lw + BQ + qo), d1 = *(const f32x4_t*)(lw + BQ + qo + 4);
+      for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          lr[8 * h2 + e] = l0[e];
-          lr[8 * h2 + 4 + e] = l1[e];
-          dr[8 * h2 + e] = d0[e];
-          dr[8 * h2 + 4 + e] = d1[e];
+          lr[4 * q4 + e] = lv[q4][e];
+          dr[4 * q4 + e] = dv4[q4][e];
         }
-      }
       float pw[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = i0 + 32 * qb + 16 * (r >> 3) + 8 * hl + (r & 7);
-        const bool hide = !kvis || lr[r] == -INFINITY || (CAUSAL && key > qi);
-        pw[r] = hide ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -lr[r]));
+        // bitwise, not short-circuit, so the test stays straight-line code
+        const bool hide = (lr[r] == -INFINITY) | (CAUSAL ? (kcut > qi) : !kvis);
+        // a hidden weight is exp2(-inf) = 0: selecting the argument keeps the
+        // exponential unconditional (a select on the result becomes a branch)
+        pw[r] = __builtin_amdgcn_exp2f(hide ? -INFINITY : fmaf(s[r], p.c, -lr[r]));
         ds[r] = pw[r] * (dp[r] - dr[r]);
       }
       bf16x8_t pp[2], pd[2];
@@ -474,20 +509,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdP
         pp[ks] = __builtin_bit_cast(bf16x8_t, w1);
         pd[ks] = __builtin_bit_cast(bf16x8_t, w2);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8 * DB, 0);
+      __builtin_amdgcn_sched_barrier(0);
       // dV^T += dO^T P and dK^T += Q^T dS (A: transpose reads; B: this lane's key)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int o0 = t_off[0][db] + (32 * qb + 16 * ks) * RB;
-          const int o1 = t_off[1][db] + (32 * qb + 16 * ks) * RB;
-          const u32x2_t d0 = lds_read_tr16(dl + o0), d1 = lds_read_tr16(dl + o1);
-          const u32x2_t q0 = lds_read_tr16(ql + o0), q1 = lds_read_tr16(ql + o1);
-          const u32x4_t ad = {d0[0], d0[1], d1[0], d1[1]};
-          const u32x4_t aq = {q0[0], q0[1], q1[0], q1[1]};
+          const u32x4_t ad = {td[ks][db][0][0], td[ks][db][0][1], td[ks][db][1][0], td[ks][db][1][1]};
+          const u32x4_t aq = {tq[ks][db][0][0], tq[ks][db][0][1], tq[ks][db][1][0], tq[ks][db][1][1]};
           dvt[db] = mfma(__builtin_bit_cast(bf16x8_t, ad), pp[ks], dvt[db]);
           dkt[db] = mfma(__builtin_bit_cast(bf16x8_t, aq), pd[ks], dkt[db]);
         }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   }
