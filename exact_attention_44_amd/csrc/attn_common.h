@@ -92,6 +92,44 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, char* ds
                                           0, 0);
 }
 
+// load16_to_lds for a buffer over [base, base + bytes), issued so that the
+// compiler does not track it. The compiler cannot tell which LDS bytes such a
+// load writes, so for a tracked load it waits for completion before any later
+// LDS read; a kernel that reads other LDS buffers meanwhile uses this form and
+// waits itself (wait_loads) before the data is read. The statement has no
+// memory clobber either: its destination is read only after a barrier that
+// follows such a wait. M0 holds the LDS
+// destination; the first s_nop covers a preceding vector write of the
+// resource's scalar registers, the second the M0 write.
+// (M0 is reserved to the compiler, which therefore does not preserve it across
+// the statement; the kernels that use this form keep nothing else in M0.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load16_to_lds_untracked(const void* base, uint32_t bytes, char* dst,
+                                                        uint32_t byte_off) {
+  const uint64_t a = (uint64_t)base;
+  u32x4_t rs;
+  rs[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  rs[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu;
+  rs[2] = __builtin_amdgcn_readfirstlane(bytes);
+  rs[3] = 0x00020000u;
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(byte_off), "s"(rs), "s"(m0)
+      : "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until every vector-memory load of this wave, untracked ones included,
+// has completed (s_waitcnt vmcnt(0)).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }

@@ -205,18 +205,22 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     k_voff = (uint32_t)((32 * grp + r) * D + 16 * (ph ^ k_swz<D>(r)));
     v_voff = (uint32_t)(key_of_slot(grp, r) * D + 16 * (ph ^ v_swz<D>(r)));
   }
+  // The tile loads are untracked by the compiler (which would otherwise wait
+  // for them before the next LDS read of any buffer); every fenced barrier
+  // below waits for them explicitly.
   auto dma_k = [&](int u) {
     const int j0 = u * BC;
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(kg + (int64_t)j0 * D, rest);
-    if (wg < N_DMA) load16_to_lds(r, lds + (u % NBUF) * BUF_BYTES + (grp * H_SLOTS + 64 * wg) * 16, k_voff);
+    if (wg < N_DMA)
+      load16_to_lds_untracked(kg + (int64_t)j0 * D, rest,
+                              lds + (u % NBUF) * BUF_BYTES + (grp * H_SLOTS + 64 * wg) * 16, k_voff);
   };
   auto dma_v = [&](int u) {
     const int j0 = u * BC;
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(vg + (int64_t)j0 * D, rest);
     if (wg < N_DMA)
-      load16_to_lds(r, lds + (u % NBUF) * BUF_BYTES + K_BYTES + (grp * H_SLOTS + 64 * wg) * 16, v_voff);
+      load16_to_lds_untracked(vg + (int64_t)j0 * D, rest,
+                              lds + (u % NBUF) * BUF_BYTES + K_BYTES + (grp * H_SLOTS + 64 * wg) * 16, v_voff);
   };
 
   // ---- per-wave running state
@@ -431,6 +435,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     dma_v(0);
     dma_v(1);
   }
+  wait_loads();
   __syncthreads();
 
   // ---- ping-pong phases, as in the bf16 kernel. Group 0 runs
@@ -443,6 +448,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   // written for tile u + 4: its K from phase 2u + 3, its V from phase 2u + 5.
   auto phase_sync = [&]() {
     __builtin_amdgcn_sched_barrier(0);
+    wait_loads();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
