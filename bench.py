@@ -59,9 +59,9 @@ MEASURED_TRAFFIC = {
         "write_bytes": 68215136,
     },
     "fp8:B=1,H=32,s=8192,d=128,causal": {
-        "source_sha256": "566b89e677657e3de75130cf2cee5350189335a2d249883655d5d55655ee2680",
-        "fetch_bytes": 203621561,
-        "write_bytes": 68166424,
+        "source_sha256": "77de391a312aa3ac80585a1fdeca2318e9563a1e145f54dfd69ffcb40698c959",
+        "fetch_bytes": 203008596,
+        "write_bytes": 68179136,
     },
 }
 
