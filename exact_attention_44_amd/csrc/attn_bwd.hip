@@ -167,6 +167,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const float Dv = dsum + __shfl_xor(dsum, 32);
   const float lse_row = row < s_q ? p.lse[(int64_t)bh * s_q + row] : -INFINITY;
   const bool live = lse_row != -INFINITY;  // a row with no visible key has P = 0
+  const bool any_dead = __ballot(!live) != 0ull;
   const float lse2 = live ? lse_row * kLog2e : 0.f;
   // D and lse*log2(e) for the dkv kernel, which loads them 64 rows at a time:
   // the rows up to the next multiple of 64 are written too (D = 0, lse = -inf,
@@ -258,17 +259,26 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
       hid = rem >= BC ? 0ull : ~((1ull << rem) - 1ull);
     }
     const int lim = row - j0;  // causal: key offset visible iff <= lim
+    // per-element masks only where the tile needs them (wave-uniform test):
+    // hidden keys, the causal diagonal, or a row with no visible key
+    const bool masked = hid != 0ull || (CAUSAL && j0 + BC - 1 > qlo) || any_dead;
     bf16x8_t pf[KB][2];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const uint32_t sh = (uint32_t)(hid >> (32 * kb)) >> (8 * hl);
       float ds[16];
+      if (masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ko = 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
-        const bool hide = !live | (((sh >> (16 * (r >> 3) + (r & 7))) & 1u) != 0u) | (CAUSAL && ko > lim);
-        const float pw = __builtin_amdgcn_exp2f(hide ? -INFINITY : fmaf(sc[kb][r], p.c, -lse2));
-        ds[r] = pw * (dp[kb][r] - Dv);
+        for (int r = 0; r < 16; ++r) {
+          const int ko = 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
+          const bool hide = !live | (((sh >> (16 * (r >> 3) + (r & 7))) & 1u) != 0u) | (CAUSAL && ko > lim);
+          const float pw = __builtin_amdgcn_exp2f(hide ? -INFINITY : fmaf(sc[kb][r], p.c, -lse2));
+          ds[r] = pw * (dp[kb][r] - Dv);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ds[r] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], p.c, -lse2)) * (dp[kb][r] - Dv);
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -350,6 +360,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdP
   // causal: this key is hidden from query qi when kcut > qi (every query
   // when the key itself is hidden)
   const int kcut = kvis ? key : INT_MAX;
+  // Without a padding mask every row below s_q sees a key (lse > -inf); with
+  // all of this wave's keys visible, only causal diagonal blocks and the
+  // ragged last block need masks.
+  const bool keys_masked = PADMASK || __ballot(!kvis) != 0ull;
+  const int kmax = k0 + 32 * wv + 31;  // this wave's last key
 
   // query tiles that can see a key of this tile
   const int qt0 = CAUSAL ? min(k0, s_q) / BQ : 0;
@@ -487,15 +502,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdP
           dr[4 * q4 + e] = dv4[q4][e];
         }
       float pw[16], ds[16];
+      // masks where a key is hidden, on the causal diagonal, and on the
+      // ragged last block (its rows past s_q carry lse = -inf)
+      if (keys_masked || (CAUSAL && i0 + 32 * qb < kmax) || i0 + 32 * qb + 32 > s_q) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = i0 + 32 * qb + 16 * (r >> 3) + 8 * hl + (r & 7);
-        // bitwise, not short-circuit, so the test stays straight-line code
-        const bool hide = (lr[r] == -INFINITY) | (CAUSAL ? (kcut > qi) : !kvis);
-        // a hidden weight is exp2(-inf) = 0: selecting the argument keeps the
-        // exponential unconditional (a select on the result becomes a branch)
-        pw[r] = __builtin_amdgcn_exp2f(hide ? -INFINITY : fmaf(s[r], p.c, -lr[r]));
-        ds[r] = pw[r] * (dp[r] - dr[r]);
+        for (int r = 0; r < 16; ++r) {
+          const int qi = i0 + 32 * qb + 16 * (r >> 3) + 8 * hl + (r & 7);
+          // bitwise, not short-circuit, so the test stays straight-line code
+          const bool hide = (lr[r] == -INFINITY) | (CAUSAL ? (kcut > qi) : !kvis);
+          // a hidden weight is exp2(-inf) = 0: selecting the argument keeps the
+          // exponential unconditional (a select on the result becomes a branch)
+          pw[r] = __builtin_amdgcn_exp2f(hide ? -INFINITY : fmaf(s[r], p.c, -lr[r]));
+          ds[r] = pw[r] * (dp[r] - dr[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pw[r] = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -lr[r]));
+          ds[r] = pw[r] * (dp[r] - dr[r]);
+        }
       }
       bf16x8_t pp[2], pd[2];
 #pragma unroll
