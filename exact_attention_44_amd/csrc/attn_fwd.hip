@@ -269,19 +269,22 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
         for (int db = 0; db < DB; ++db) o[db] = mfma(a[db], pf[kb][ks], o[db]);
       }
   };
-  // M step, second half: S(t)^T = K_t Q^T.
+  // M step, second half: S(t)^T = K_t Q^T. The key blocks' accumulation
+  // chains are interleaved (k-step outer), so consecutive MFMAs never depend
+  // on each other's result.
   auto qk = [&](int t) {
     const char* kl = lds + (t % NBUF) * BUF_BYTES + k_lane_off;
+    f32x16_t acc[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bf16x8_t a[DK];
+    for (int kk = 0; kk < DK; ++kk) {
+      bf16x8_t a[KB];
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) a[kk] = *(const bf16x8_t*)(kl + kb * 32 * KS + kk * 32);
-      f32x16_t acc = {};
+      for (int kb = 0; kb < KB; ++kb) a[kb] = *(const bf16x8_t*)(kl + kb * 32 * KS + kk * 32);
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) acc = mfma(a[kk], qf[kk], acc);
-      sc[kb] = acc;
+      for (int kb = 0; kb < KB; ++kb) acc[kb] = mfma(a[kb], qf[kk], kk ? acc[kb] : f32x16_t{});
     }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sc[kb] = acc[kb];
     if (PADMASK) {
       const int key = t * BC + lane;
       mbyte = key < s_kc ? (uint32_t)mg[key] : 1u;
