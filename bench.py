@@ -54,9 +54,9 @@ KERNEL_SOURCE_FP8 = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_f
 # source they were taken on: reported as null once the source's hash differs.
 MEASURED_TRAFFIC = {
     "B=1,H=32,s=8192,d=128,causal": {
-        "source_sha256": "76d3b683251bc9eb7c6fb8f4100e6df415a46de4c057c96ea4acef7048e45143",
-        "fetch_bytes": 492803164,
-        "write_bytes": 68215136,
+        "source_sha256": "b6e180b8d2d13535a8e600726c0d427cabf2178cc0d47d50a1f9b5ed795ca8fe",
+        "fetch_bytes": 504661763,
+        "write_bytes": 68202080,
     },
     "fp8:B=1,H=32,s=8192,d=128,causal": {
         "source_sha256": "77de391a312aa3ac80585a1fdeca2318e9563a1e145f54dfd69ffcb40698c959",
