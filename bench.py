@@ -50,13 +50,15 @@ KERNEL_SOURCE_FP8 = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_f
 
 # HBM bytes per launch from two rocprofv3 counter passes (FETCH_SIZE, then
 # WRITE_SIZE) of this script, each scaled by what the same counter reports for
-# a 1 GiB copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0). Valid only for the kernel
-# source they were taken on: reported as null once the source's hash differs.
+# a 1 GiB copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the mean over the
+# launches after the first (the first runs with cold caches, the timed
+# launches run back to back). Valid only for the kernel source they were taken
+# on: reported as null once the source's hash differs.
 MEASURED_TRAFFIC = {
     "B=1,H=32,s=8192,d=128,causal": {
-        "source_sha256": "b6e180b8d2d13535a8e600726c0d427cabf2178cc0d47d50a1f9b5ed795ca8fe",
-        "fetch_bytes": 504661763,
-        "write_bytes": 68202080,
+        "source_sha256": "f778fed4977fccd26a420a7547bc14011569d11d877b1927d3201de6458da7f0",
+        "fetch_bytes": 486749803,
+        "write_bytes": 68271840,
     },
     "fp8:B=1,H=32,s=8192,d=128,causal": {
         "source_sha256": "77de391a312aa3ac80585a1fdeca2318e9563a1e145f54dfd69ffcb40698c959",

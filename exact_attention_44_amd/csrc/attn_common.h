@@ -66,6 +66,26 @@ __device__ __forceinline__ i32x2_t lds_read_tr8(const char* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)p);
 }
 
+// XOR applied to the 16-byte slot index of row r of a 64-row bf16 tile in LDS
+// (V in the forward, K and V in the backward's dq kernel, Q and dO in its dkv
+// kernel; unpadded rows of 2D bytes; it depends on r mod 16 only). The score-side
+// reads take one slot of 16 rows (a permutation of an aligned group of 16);
+// the transpose reads take 4 adjacent slots of 4 adjacent rows per half wave;
+// with this permutation both kinds of read hit distinct banks.
+template <int D>
+__device__ __forceinline__ int q_swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 2) << 1) | ((r >> 2) & 3));
+}
+
+// 16-bit LDS transpose read: within each group of 16 lanes, element k (0..3)
+// of lane i = 4j + c comes from the address given by lane 4k + j of the
+// group, plus c elements.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const char* p) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2_t f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));

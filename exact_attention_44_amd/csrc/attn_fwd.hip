@@ -25,9 +25,15 @@
 // a bf16 conversion only. The output accumulator O^T has one query row per
 // lane too, so the rescale by exp(m_old - m_new) is a per-lane scalar.
 //
-// LDS: K tile row-major [BC][D], V tile transposed [D][BC] (the transpose is
-// done in registers while storing), rows padded by 16 bytes so every 16-lane
-// fragment read hits distinct banks. Four buffers. The two wave groups take
+// LDS: K tile row-major [BC][D] with rows padded by 16 bytes, so every
+// 16-lane fragment read hits distinct banks, loaded from memory straight into
+// LDS (buffer loads with LDS as the destination). At D = 128 the V tile is
+// loaded the same way, row-major [BC][D] with unpadded rows whose 16-byte
+// slots are XOR-swizzled per row, and read as the transposed operand V^T by
+// 16-bit LDS transpose reads. At D = 64 the V tile passes through registers
+// and is stored transposed, [D][BC] with padded rows, and read by plain
+// fragment reads: the transpose reads, two per fragment, cost more there
+// than the register transpose. Four buffers. The two wave groups take
 // turns (ping-pong): while one group's waves run the matrix products, the
 // other group's waves run the softmax, and each SIMD holds one wave of each
 // group, because a wave's own vector instructions do not overlap its own
@@ -75,25 +81,32 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // LDS rows are padded by 16 bytes: with these strides the 16 lanes of every
   // fragment read hit 16 distinct 4-bank groups, and each lane's fragment
   // addresses are one base plus compile-time offsets.
+  constexpr bool VDMA = D == 128;     // V by load-to-LDS and transpose reads
   constexpr int KS = D * 2 + 16;      // K row stride (bytes)
-  constexpr int VS = BC * 2 + 16;     // V^T row stride (bytes)
+  constexpr int RB = D * 2;           // V row stride with VDMA (unpadded, swizzled slots)
+  constexpr int VS = BC * 2 + 16;     // V^T row stride otherwise (bytes)
   constexpr int K_BYTES = BC * KS;
-  constexpr int BUF_BYTES = K_BYTES + D * VS;
+  constexpr int BUF_BYTES = K_BYTES + (VDMA ? BC * RB : D * VS);
   constexpr int NBUF = 4;             // see the phase schedule below
   // Each group stages its half (32 keys) of a tile. K goes from memory
   // straight into its padded LDS rows (buffer loads with LDS as the
   // destination): the half is 32 rows of ROW_SLOTS 16-byte slots, written by
   // K_DMA instructions of 64 consecutive slots each; the last instruction
   // overlaps its predecessor, so the overlap is written twice with the same
-  // data, and a padding slot receives its row's first 16 bytes. V goes
-  // through registers in items of 2 keys x 8 columns, transposed on the way
-  // into LDS.
+  // data, and a padding slot receives its row's first 16 bytes. With VDMA,
+  // V's half is 32 unpadded rows of D / 8 slots, V_DMA_W instructions per
+  // wave, and LDS slot p of row r holds the row's 16-byte unit p ^ q_swz(r);
+  // otherwise V goes through registers in items of 2 keys x 8 columns,
+  // transposed on the way into LDS.
   constexpr int GT = NT / 2;
   constexpr int ROW_SLOTS = KS / 16;
   constexpr int K_SLOTS = 32 * ROW_SLOTS;
   constexpr int K_DMA = (K_SLOTS + 63) / 64;
   constexpr int K_DMA_W = (K_DMA + 3) / 4;  // per wave, at most
   static_assert(K_SLOTS >= 64, "a half tile must fill one DMA instruction");
+  constexpr int V_SLOTS = 32 * KU;
+  constexpr int V_DMA_W = V_SLOTS / 64 / 4;
+  static_assert(V_DMA_W * 64 * 4 == V_SLOTS, "a V half tile is a whole number of DMA rounds");
   constexpr int V_ITEMS = 16 * (D / 8);
   constexpr int V_LD = (V_ITEMS + GT - 1) / GT;
   constexpr float kSumLimit = 1048576.f;  // 2^20: see the softmax phase
@@ -194,6 +207,24 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       }
     }
   };
+  uint32_t v_voff[V_DMA_W];
+#pragma unroll
+  for (int i = 0; i < V_DMA_W; ++i) {
+    const int sl = 64 * (4 * i + wg) + lane;
+    const int r = 32 * grp + sl / KU, un = sl % KU;
+    v_voff[i] = (uint32_t)(r * RB + 16 * (un ^ q_swz<D>(r)));
+  }
+  // V rows of tile u into LDS, the same way as K (VDMA).
+  auto dma_v = [&](int u) {
+    const int j0 = u * BC;
+    const uint32_t rest = (uint32_t)max(s_kc - j0, 0) * D * 2;
+    const __amdgpu_buffer_rsrc_t rvt = make_rsrc(vg + (int64_t)j0 * D, rest);
+    char* vl = lds + (u % NBUF) * BUF_BYTES + K_BYTES + grp * V_SLOTS * 16;
+#pragma unroll
+    for (int i = 0; i < V_DMA_W; ++i) load16_to_lds(rvt, vl + 64 * (4 * i + wg) * 16, v_voff[i]);
+  };
+  // V through registers (not VDMA): load_v(u) fetches this thread's item of
+  // tile u, store_v(u) writes it transposed.
   u32x4_t vr[V_LD][2];
   auto load_v = [&](int u) {
     const int j0 = u * BC;
@@ -239,7 +270,21 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16_t{};
 
   const int k_lane_off = key_of_row(ln) * KS + hl * 16;
-  const int v_lane_off = ln * VS + hl * 16;
+  // VDMA: transpose-read offsets of V^T: read r (0, 1) of feature block db
+  // gives keys 8 hl + 4 r .. +3 of a 16-key step for feature 32 db + ln
+  const int v_lane_off = ln * VS + hl * 16;  // not VDMA
+  int t_off[2][DB];
+  {
+    const int a = lane & 15, g = (lane >> 4) & 1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int rw = 8 * hl + 4 * r + (a >> 2);
+        const int slot = 4 * db + 2 * g + ((a & 3) >> 1);
+        t_off[r][db] = rw * RB + 16 * (slot ^ q_swz<D>(rw)) + 8 * (a & 1);
+      }
+  }
   const float c = p.c;
 
   // The first LA fragments of each value product are read at the end of the
@@ -249,9 +294,17 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   bf16x8_t vpre[LA];
   auto v_frag = [&](int t, int i) -> bf16x8_t {
     // fragment i of tile t's value product: kb = i / 8, ks = (i / 4) & 1, db = i & 3
-    const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + v_lane_off;
-    const int kb = i / (2 * DB), ks = (i / DB) & 1, db = i % DB;
-    return *(const bf16x8_t*)(vl + db * 32 * VS + (4 * kb + 2 * ks) * 16);
+    const int db = i % DB;
+    if constexpr (VDMA) {
+      const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + (16 * (i / DB)) * RB;
+      const u32x2_t lo = lds_read_tr16(vl + t_off[0][db]);
+      const u32x2_t hi = lds_read_tr16(vl + t_off[1][db]);
+      const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+      return __builtin_bit_cast(bf16x8_t, w);
+    } else {
+      const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + v_lane_off;
+      return *(const bf16x8_t*)(vl + db * 32 * VS + (i / DB) * 32);
+    }
   };
   // M step, first half: O^T += V_t^T P(t)^T (tile t in LDS buffer t % NBUF).
   auto pv = [&](int t) {
@@ -292,17 +345,27 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   };
   // One M step: value product of tile tp, then score product of tile tq,
   // software-pipelined so LDS fragment reads run LA fragments ahead of the
-  // MFMAs that consume them (an LDS read takes several MFMA durations).
-  constexpr int N_MF = KB * 2 * DB + KB * DK;  // MFMAs (= fragment reads) per M step
-  static_assert(LA <= 2 * DB * KB, "prefetched fragments must belong to the value product");
+  // MFMAs that consume them (an LDS read takes several MFMA durations). With
+  // VDMA a value-product fragment takes two transpose reads; otherwise every
+  // fragment is one read, and the M step also stages V.
+  constexpr int N_PV = KB * 2 * DB;            // value-product MFMAs per M step
+  constexpr int N_MF = N_PV + KB * DK;         // MFMAs (= fragments) per M step
+  static_assert(LA <= N_PV, "prefetched fragments must belong to the value product");
   auto m_step = [&](int tp, int tq) {
     __builtin_amdgcn_s_setprio(2);
     pv(tp);
     qk(tq);
-    store_v(tq + 1);
-    load_v(tq + 2);
+    if constexpr (!VDMA) {
+      store_v(tq + 1);
+      load_v(tq + 2);
+    }
 #pragma unroll
-    for (int i = 0; i < N_MF - LA; ++i) {
+    for (int i = 0; i < N_PV - LA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, VDMA ? 2 : 1, 0);  // DS read(s)
+    }
+#pragma unroll
+    for (int i = N_PV - LA; i < N_MF - LA; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
@@ -313,6 +376,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // V step: masks and online softmax of S(t) -> P(t).
   auto vstep = [&](int t) {
     dma_k(t + 3);
+    if constexpr (VDMA) dma_v(t + 2);
     const int j0 = t * BC;
     // hidden-key bits of the tile (padding, keys past s_k); wave-uniform
     uint64_t hid;
@@ -415,26 +479,33 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     dma_k(0);
     dma_k(1);
     dma_k(2);
-    load_v(0);
-    store_v(0);
-    load_v(1);
-    store_v(1);
-    load_v(2);
+    if constexpr (VDMA) {
+      dma_v(0);
+      dma_v(1);
+    } else {
+      load_v(0);
+      store_v(0);
+      load_v(1);
+      store_v(1);
+      load_v(2);
+    }
   }
   __syncthreads();
 
   // ---- ping-pong phases (2 * n_kv + 2, each closed by a barrier). Group 0
   // runs  M(0) V(0) M(1) V(1) ... V(n-1) M(n),  group 1 the same one phase
-  // later, where M(t) = [PV(t-1), QK(t), V staging] issues the matrix-core
-  // work and V(t) = [K staging, softmax of S(t)] the vector-ALU work. Waves w
+  // later, where M(t) = [PV(t-1), QK(t)] issues the matrix-core work and
+  // V(t) = [K staging, softmax of S(t)] the vector-ALU work; V is staged by
+  // load-to-LDS in V steps (VDMA) or through registers in M steps. Waves w
   // and w + 4 share a SIMD, so every SIMD holds one wave in an M step and one
-  // in a V step and the two units overlap. The staging is split between the
-  // two kinds of step so that they take about equally long. LDS buffer
-  // u % 4 holds tile u: its K half is written in phases 2u - 3 (group 0) and
-  // 2u - 2 (group 1) and read by QK(u) in phases 2u, 2u + 1; its V half is
-  // written in phases 2u - 2, 2u - 1 and read by PV(u) in phases 2u + 1 ..
-  // 2u + 3 (from the prefetch at the end of V(u) on). Both halves are free
-  // again before tile u + 4 is written, from phase 2u + 5 on.
+  // in a V step and the two units overlap. LDS buffer u % 4 holds tile u:
+  // its K part is written in phases 2u - 5 (group 0) and 2u - 4 (group 1)
+  // and read by QK(u) in phases 2u, 2u + 1; its V part is written in phases
+  // 2u - 3, 2u - 2 (VDMA, by V(u - 2)) or 2u - 2, 2u - 1 (stores in
+  // M(u - 1)) and read by PV(u) in phases 2u + 1 .. 2u + 3 (from the
+  // prefetch at the end of V(u) on). Each write lands after the last read of
+  // tile u - 4 (K: phase 2u - 7, V: phase 2u - 5), and the fenced barrier
+  // that closes the writing wave's next M step waits for it.
   // Phase boundary. The barrier orders memory only; the scheduling fences on
   // both sides also keep register-only work in its phase (otherwise the
   // compiler sinks the softmax into the next M step to fill MFMA gaps, and
@@ -445,9 +516,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
   // Phase boundary after V(t). The V step writes no LDS through its own
-  // stores (its K tile arrives by DMA, which the fenced barrier at the end of
-  // the next M step waits for, long before the tile is read), so this barrier
-  // needs no memory fence; the first LA fragments of PV(t) are requested
+  // stores (its tiles arrive by DMA, which the fenced barrier at the end of
+  // the next M step waits for, long before the tiles are read), so this
+  // barrier needs no memory fence; the first LA fragments of PV(t) are requested
   // right before it, and their latency overlaps the barrier wait. V tile t is
   // not written again before PV(t) has read it.
   auto vstep_sync = [&](int t) {
