@@ -37,8 +37,8 @@
 // turns (ping-pong): while one group's waves run the matrix products, the
 // other group's waves run the softmax, and each SIMD holds one wave of each
 // group, because a wave's own vector instructions do not overlap its own
-// MFMAs while those of another wave on the SIMD do. Phases are separated by
-// workgroup barriers.
+// MFMAs while those of another wave on the SIMD do. One workgroup barrier
+// per key tile keeps the groups in step.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int VS = BC * 2 + 16;     // V^T row stride otherwise (bytes)
   constexpr int K_BYTES = BC * KS;
   constexpr int BUF_BYTES = K_BYTES + (VDMA ? BC * RB : D * VS);
-  constexpr int NBUF = 4;             // see the phase schedule below
+  constexpr int NBUF = 4;             // see the schedule below
   // Each group stages its half (32 keys) of a tile. K goes from memory
   // straight into its padded LDS rows (buffer loads with LDS as the
   // destination): the half is 32 rows of ROW_SLOTS 16-byte slots, written by
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   static_assert(V_DMA_W * 64 * 4 == V_SLOTS, "a V half tile is a whole number of DMA rounds");
   constexpr int V_ITEMS = 16 * (D / 8);
   constexpr int V_LD = (V_ITEMS + GT - 1) / GT;
-  constexpr float kSumLimit = 1048576.f;  // 2^20: see the softmax phase
+  constexpr float kSumLimit = 1048576.f;  // 2^20: see the V step
 
   __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF_BYTES];
   __shared__ int lds_last;
@@ -263,8 +263,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
-  f32x16_t sc[KB];         // scores of the tile between its two phases
-  bf16x8_t pf[KB][2];      // weights of the tile between its two phases
+  f32x16_t sc[KB];         // scores of the tile between its two steps
+  bf16x8_t pf[KB][2];      // weights of the tile between its two steps
   uint32_t mbyte = 1u;     // this lane's padding byte of the tile in flight
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16_t{};
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   const float c = p.c;
 
   // The first LA fragments of each value product are read at the end of the
-  // V step before it (see vstep_sync), so the M step starts on data that is
+  // V step before it (see vstep_end), so the M step starts on data that is
   // already in registers instead of waiting for the LDS latency.
   constexpr int LA = 6;               // fragment reads in flight in an M step
   bf16x8_t vpre[LA];
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
-    __builtin_amdgcn_sched_barrier(0);  // keep the M step inside its phase
+    __builtin_amdgcn_sched_barrier(0);  // keep the M step in one piece
     __builtin_amdgcn_s_setprio(0);
   };
   // V step: masks and online softmax of S(t) -> P(t).
@@ -492,76 +492,71 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   }
   __syncthreads();
 
-  // ---- ping-pong phases (2 * n_kv + 2, each closed by a barrier). Group 0
-  // runs  M(0) V(0) M(1) V(1) ... V(n-1) M(n),  group 1 the same one phase
-  // later, where M(t) = [PV(t-1), QK(t)] issues the matrix-core work and
-  // V(t) = [K staging, softmax of S(t)] the vector-ALU work; V is staged by
-  // load-to-LDS in V steps (VDMA) or through registers in M steps. Waves w
-  // and w + 4 share a SIMD, so every SIMD holds one wave in an M step and one
-  // in a V step and the two units overlap. LDS buffer u % 4 holds tile u:
-  // its K part is written in phases 2u - 5 (group 0) and 2u - 4 (group 1)
-  // and read by QK(u) in phases 2u, 2u + 1; its V part is written in phases
-  // 2u - 3, 2u - 2 (VDMA, by V(u - 2)) or 2u - 2, 2u - 1 (stores in
-  // M(u - 1)) and read by PV(u) in phases 2u + 1 .. 2u + 3 (from the
-  // prefetch at the end of V(u) on). Each write lands after the last read of
-  // tile u - 4 (K: phase 2u - 7, V: phase 2u - 5), and the fenced barrier
-  // that closes the writing wave's next M step waits for it.
-  // Phase boundary. The barrier orders memory only; the scheduling fences on
-  // both sides also keep register-only work in its phase (otherwise the
-  // compiler sinks the softmax into the next M step to fill MFMA gaps, and
-  // each wave ends up doing both kinds of work serially).
+  // ---- ping-pong schedule: n_kv + 2 intervals, each closed by a workgroup
+  // barrier. M(t) = [PV(t-1), QK(t)] issues matrix-core work, V(t) =
+  // [K (and, VDMA, V) staging, softmax of S(t)] vector-ALU work. Interval 0:
+  // group 0 runs QK(0). Interval t + 1 (t < n_kv): group 0 runs V(t) then
+  // M(t + 1), group 1 runs M(t) then V(t) (M(n_kv) is PV(n_kv - 1) alone).
+  // Interval n_kv + 1: group 1 runs PV(n_kv - 1). Waves w and w + 4 share a
+  // SIMD, so while one is in its M step the other is in its V step and the
+  // two units overlap; within an interval the two waves switch kinds without
+  // a barrier, which saves one barrier per tile over a barrier at every
+  // switch.
+  // LDS buffer u % 4 holds tile u. Its K part is written (by load-to-LDS
+  // in V(u - 3)) in interval u - 2 and read by QK(u) in intervals u (group
+  // 0) and u + 1 (group 1). Its V part is written in interval u - 1 (VDMA:
+  // load-to-LDS in V(u - 2); otherwise stores in M(u - 1), group 0 in
+  // interval u - 1 and group 1 in interval u) and read from the prefetch at
+  // the end of V(u) (interval u + 1) to PV(u) of group 1 (interval u + 2).
+  // So every write comes after the last read of tile u - 4 (K: interval
+  // u - 3, V: interval u - 2), and the fenced barrier closing the interval of
+  // a write waits for it (loads into LDS included) before any read.
+  // The scheduling fences also keep register-only work in its step
+  // (otherwise the compiler sinks the softmax into the next M step to fill
+  // MFMA gaps, and each wave ends up doing both kinds of work serially).
   auto phase_sync = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Phase boundary after V(t). The V step writes no LDS through its own
-  // stores (its tiles arrive by DMA, which the fenced barrier at the end of
-  // the next M step waits for, long before the tiles are read), so this
-  // barrier needs no memory fence; the first LA fragments of PV(t) are requested
-  // right before it, and their latency overlaps the barrier wait. V tile t is
-  // not written again before PV(t) has read it.
-  auto vstep_sync = [&](int t) {
+  // End of V(t): the first LA fragments of PV(t) are requested here, so their
+  // latency overlaps the switch to the M step.
+  auto vstep_end = [&](int t) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < LA; ++i) vpre[i] = v_frag(t, i);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
   };
-  if (grp == 0) {
-    if (n_kv > 0) qk(0);
-    phase_sync();
-    for (int t = 0; t < n_kv - 1; ++t) {
-      vstep(t);
-      vstep_sync(t);
-      m_step(t, t + 1);
+  if (n_kv > 0) {
+    if (grp == 0) {
+      qk(0);
       phase_sync();
-    }
-    if (n_kv > 0) {
+      for (int t = 0; t < n_kv - 1; ++t) {
+        vstep(t);
+        vstep_end(t);
+        m_step(t, t + 1);
+        phase_sync();
+      }
       vstep(n_kv - 1);
-      vstep_sync(n_kv - 1);
+      vstep_end(n_kv - 1);
+      pv(n_kv - 1);
+      phase_sync();
+      phase_sync();
+    } else {
+      phase_sync();
+      qk(0);
+      vstep(0);
+      vstep_end(0);
+      phase_sync();
+      for (int t = 1; t < n_kv; ++t) {
+        m_step(t - 1, t);
+        vstep(t);
+        vstep_end(t);
+        phase_sync();
+      }
       pv(n_kv - 1);
       phase_sync();
     }
-    phase_sync();
-  } else {
-    phase_sync();  // phase 0: group 0 alone
-    if (n_kv > 0) {
-      qk(0);
-      phase_sync();
-      vstep(0);
-      vstep_sync(0);
-    }
-    for (int t = 1; t < n_kv; ++t) {
-      m_step(t - 1, t);
-      phase_sync();
-      vstep(t);
-      vstep_sync(t);
-    }
-    if (n_kv > 0) pv(n_kv - 1);
-    phase_sync();
   }
 
   // ---- epilogue: O = O^T / l, lse = m * |scale| + ln(l)
