@@ -13,9 +13,9 @@
 //
 // Decomposition and schedule follow the bf16 kernel: one workgroup per
 // (b, h, 256 query rows), 8 waves of 32 rows, waves w and w + 4 on one SIMD,
-// the two groups of four alternating matrix phases (value product of the
-// previous tile, score product of this one) and vector phases (masks and
-// softmax), separated by workgroup barriers.
+// the two groups of four alternating matrix steps (value product of the
+// previous tile, score product of this one) and vector steps (masks and
+// softmax), one workgroup barrier per key tile.
 //
 // Operand layouts. Scores are computed transposed, S^T = K Q^T: A = 32 keys x
 // 64 features (K rows in their natural order), B = 64 features x 32 queries
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t sc[KB];
-  float xw[KB][16];        // float32 weights of the tile between its two phases
+  float xw[KB][16];        // float32 weights of the tile between its two steps
   i32x8_t pf;              // the same rounded to E4M3 (value product operand)
   uint32_t mbyte = 1u;
 #pragma unroll
@@ -438,70 +438,65 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   wait_loads();
   __syncthreads();
 
-  // ---- ping-pong phases, as in the bf16 kernel. Group 0 runs
-  // QK(0) V(0) M(0,1) V(1) ... V(n-1) PV(n-1), group 1 the same one phase
-  // later. LDS buffer u % 4 holds tile u. K(u) is requested in the V steps of
-  // phases 2u - 5 (group 0) and 2u - 4 (group 1), V(u) in phases 2u - 3 and
-  // 2u - 2; the fenced barrier at the end of the requesting wave's next M
-  // step waits for them. K(u) is read by QK(u) in phases 2u, 2u + 1; V(u) by
-  // PV(u) from the end of phase 2u + 1 to phase 2u + 3. Buffer u % 4 is next
-  // written for tile u + 4: its K from phase 2u + 3, its V from phase 2u + 5.
+  // ---- ping-pong schedule, as in the bf16 kernel: n_kv + 2 intervals, each
+  // closed by a workgroup barrier. Interval 0: group 0 runs QK(0). Interval
+  // t + 1 (t < n_kv): group 0 runs V(t) then M(t + 1), group 1 M(t) then V(t)
+  // (M(n_kv) is PV(n_kv - 1) alone). Interval n_kv + 1: group 1 runs
+  // PV(n_kv - 1). LDS buffer u % 4 holds tile u. K(u) is requested by V(u - 3)
+  // in interval u - 2 and read by QK(u) in intervals u (group 0) and u + 1
+  // (group 1); V(u) is requested by V(u - 2) in interval u - 1 and read from
+  // the prefetch at the end of V(u) (interval u + 1) to PV(u) of group 1
+  // (interval u + 2). Every request comes after the last read of tile u - 4
+  // (K: interval u - 3, V: interval u - 2) and is waited for (explicitly: the
+  // requests are untracked) at the barrier closing its interval.
   auto phase_sync = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     wait_loads();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // After a V step: issue the first LA reads of PV(t), then a bare barrier
-  // (this step wrote no LDS through stores; its DMA is waited for at the next
-  // fenced barrier, long before the data is read).
-  auto vstep_sync = [&](int t) {
+  // End of V(t): the first LA reads of PV(t) are issued here, so their
+  // latency overlaps the switch to the M step.
+  auto vstep_end = [&](int t) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < LA; ++i) vpre[i] = v_read(t, i);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
   };
-  if (grp == 0) {
-    if (n_kv > 0) qk(0);
-    phase_sync();
-    for (int t = 0; t < n_kv - 1; ++t) {
-      vstep(t);
-      vstep_sync(t);
-      m_step(t, t + 1);
-      phase_sync();
-    }
-    if (n_kv > 0) {
-      vstep(n_kv - 1);
-      vstep_sync(n_kv - 1);
-      read_v(n_kv - 1);
-      finish();
-      pv_mfma();
-      phase_sync();
-    }
-    phase_sync();
-  } else {
-    phase_sync();
-    if (n_kv > 0) {
+  if (n_kv > 0) {
+    if (grp == 0) {
       qk(0);
       phase_sync();
-      vstep(0);
-      vstep_sync(0);
-    }
-    for (int t = 1; t < n_kv; ++t) {
-      m_step(t - 1, t);
-      phase_sync();
-      vstep(t);
-      vstep_sync(t);
-    }
-    if (n_kv > 0) {
+      for (int t = 0; t < n_kv - 1; ++t) {
+        vstep(t);
+        vstep_end(t);
+        m_step(t, t + 1);
+        phase_sync();
+      }
+      vstep(n_kv - 1);
+      vstep_end(n_kv - 1);
       read_v(n_kv - 1);
       finish();
       pv_mfma();
+      phase_sync();
+      phase_sync();
+    } else {
+      phase_sync();
+      qk(0);
+      vstep(0);
+      vstep_end(0);
+      phase_sync();
+      for (int t = 1; t < n_kv; ++t) {
+        m_step(t - 1, t);
+        vstep(t);
+        vstep_end(t);
+        phase_sync();
+      }
+      read_v(n_kv - 1);
+      finish();
+      pv_mfma();
+      phase_sync();
     }
-    phase_sync();
   }
 
   // ---- epilogue: O = dv * O^T / l, lse = m |scale dq dk| + ln(l)
