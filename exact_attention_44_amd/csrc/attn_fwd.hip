@@ -28,9 +28,10 @@
 // LDS: K tile row-major [BC][D] with rows padded by 16 bytes, so every
 // 16-lane fragment read hits distinct banks, loaded from memory straight into
 // LDS (buffer loads with LDS as the destination). At D = 128 the V tile is
-// loaded the same way, row-major [BC][D] with unpadded rows whose 16-byte
-// slots are XOR-swizzled per row, and read as the transposed operand V^T by
-// 16-bit LDS transpose reads. At D = 64 the V tile passes through registers
+// loaded the same way, row-major [BC][D] with rows padded by 64 bytes, and
+// read as the transposed operand V^T by 16-bit LDS transpose reads (the
+// padding puts the four rows each half wave reads on disjoint banks, and
+// keeps every lane's read addresses one base plus compile-time offsets). At D = 64 the V tile passes through registers
 // and is stored transposed, [D][BC] with padded rows, and read by plain
 // fragment reads: the transpose reads, two per fragment, cost more there
 // than the register transpose. Four buffers. The two wave groups take
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // addresses are one base plus compile-time offsets.
   constexpr bool VDMA = D == 128;     // V by load-to-LDS and transpose reads
   constexpr int KS = D * 2 + 16;      // K row stride (bytes)
-  constexpr int RB = D * 2;           // V row stride with VDMA (unpadded, swizzled slots)
+  constexpr int RB = D * 2 + 64;      // V row stride with VDMA (bytes)
   constexpr int VS = BC * 2 + 16;     // V^T row stride otherwise (bytes)
   constexpr int K_BYTES = BC * KS;
   constexpr int BUF_BYTES = K_BYTES + (VDMA ? BC * RB : D * VS);
@@ -94,8 +95,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // K_DMA instructions of 64 consecutive slots each; the last instruction
   // overlaps its predecessor, so the overlap is written twice with the same
   // data, and a padding slot receives its row's first 16 bytes. With VDMA,
-  // V's half is 32 unpadded rows of D / 8 slots, V_DMA_W instructions per
-  // wave, and LDS slot p of row r holds the row's 16-byte unit p ^ q_swz(r);
+  // V's half is 32 rows of RB / 16 slots, written by V_DMA instructions of
+  // 64 consecutive slots (a padding slot receives its row's first 16 bytes);
   // otherwise V goes through registers in items of 2 keys x 8 columns,
   // transposed on the way into LDS.
   constexpr int GT = NT / 2;
@@ -104,9 +105,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int K_DMA = (K_SLOTS + 63) / 64;
   constexpr int K_DMA_W = (K_DMA + 3) / 4;  // per wave, at most
   static_assert(K_SLOTS >= 64, "a half tile must fill one DMA instruction");
-  constexpr int V_SLOTS = 32 * KU;
-  constexpr int V_DMA_W = V_SLOTS / 64 / 4;
-  static_assert(V_DMA_W * 64 * 4 == V_SLOTS, "a V half tile is a whole number of DMA rounds");
+  constexpr int V_ROW_SLOTS = RB / 16;
+  constexpr int V_SLOTS = 32 * V_ROW_SLOTS;
+  constexpr int V_DMA = V_SLOTS / 64;
+  constexpr int V_DMA_W = (V_DMA + 3) / 4;  // per wave, at most
+  static_assert(V_DMA * 64 == V_SLOTS, "a V half tile is a whole number of DMA instructions");
   constexpr int V_ITEMS = 16 * (D / 8);
   constexpr int V_LD = (V_ITEMS + GT - 1) / GT;
   constexpr float kSumLimit = 1048576.f;  // 2^20: see the V step
@@ -207,12 +210,15 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       }
     }
   };
+  // V instructions are dealt starting one wave after K's, so the group's
+  // waves issue equal numbers of loads (within one).
   uint32_t v_voff[V_DMA_W];
 #pragma unroll
   for (int i = 0; i < V_DMA_W; ++i) {
-    const int sl = 64 * (4 * i + wg) + lane;
-    const int r = 32 * grp + sl / KU, un = sl % KU;
-    v_voff[i] = (uint32_t)(r * RB + 16 * (un ^ q_swz<D>(r)));
+    const int j = ((wg + 3) & 3) + 4 * i;
+    const int slot = 64 * min(j, V_DMA - 1) + lane;
+    const int r = 32 * grp + slot / V_ROW_SLOTS, un = slot % V_ROW_SLOTS;
+    v_voff[i] = (uint32_t)(r * D + (un < KU ? 8 * un : 0)) * 2;
   }
   // V rows of tile u into LDS, the same way as K (VDMA).
   auto dma_v = [&](int u) {
@@ -221,7 +227,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     const __amdgpu_buffer_rsrc_t rvt = make_rsrc(vg + (int64_t)j0 * D, rest);
     char* vl = lds + (u % NBUF) * BUF_BYTES + K_BYTES + grp * V_SLOTS * 16;
 #pragma unroll
-    for (int i = 0; i < V_DMA_W; ++i) load16_to_lds(rvt, vl + 64 * (4 * i + wg) * 16, v_voff[i]);
+    for (int i = 0; i < V_DMA_W; ++i) {
+      const int j = ((wg + 3) & 3) + 4 * i;
+      if (j < V_DMA) load16_to_lds(rvt, vl + 64 * j * 16, v_voff[i]);
+    }
   };
   // V through registers (not VDMA): load_v(u) fetches this thread's item of
   // tile u, store_v(u) writes it transposed.
@@ -270,21 +279,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16_t{};
 
   const int k_lane_off = key_of_row(ln) * KS + hl * 16;
-  // VDMA: transpose-read offsets of V^T: read r (0, 1) of feature block db
-  // gives keys 8 hl + 4 r .. +3 of a 16-key step for feature 32 db + ln
-  const int v_lane_off = ln * VS + hl * 16;  // not VDMA
-  int t_off[2][DB];
-  {
-    const int a = lane & 15, g = (lane >> 4) & 1;
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int rw = 8 * hl + 4 * r + (a >> 2);
-        const int slot = 4 * db + 2 * g + ((a & 3) >> 1);
-        t_off[r][db] = rw * RB + 16 * (slot ^ q_swz<D>(rw)) + 8 * (a & 1);
-      }
-  }
+  // VDMA: transpose-read offset of V^T: read r (0, 1) of feature block db
+  // gives keys 8 hl + 4 r .. +3 of a 16-key step for feature 32 db + ln, at
+  // v_lane_off + r * 4 * RB + db * 64
+  const int v_lane_off = VDMA ? (8 * hl + ((lane & 15) >> 2)) * RB + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1)
+                              : ln * VS + hl * 16;
   const float c = p.c;
 
   // The first LA fragments of each value product are read at the end of the
@@ -296,9 +295,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     // fragment i of tile t's value product: kb = i / 8, ks = (i / 4) & 1, db = i & 3
     const int db = i % DB;
     if constexpr (VDMA) {
-      const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + (16 * (i / DB)) * RB;
-      const u32x2_t lo = lds_read_tr16(vl + t_off[0][db]);
-      const u32x2_t hi = lds_read_tr16(vl + t_off[1][db]);
+      const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + v_lane_off + (16 * (i / DB)) * RB + db * 64;
+      const u32x2_t lo = lds_read_tr16(vl);
+      const u32x2_t hi = lds_read_tr16(vl + 4 * RB);
       const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
       return __builtin_bit_cast(bf16x8_t, w);
     } else {
