@@ -61,6 +61,7 @@ struct FwdParams {
   float* lse;
   const uint8_t* kpm;
   int s_q, s_k, H, BH, n_qt;
+  int n_items;      // work items: key chunks x query tiles x (b, h)
   int k_chunk;      // keys per chunk of a key-split launch (a multiple of 64)
   float* o_part;    // key-split partial outputs, fp32 [chunk][B*H][s_q][d]
   float* lse_part;  // key-split partial log-sum-exps, fp32 [chunk][B*H][s_q]
@@ -125,65 +126,71 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   const int hl = lane >> 5;
   const int ln = lane & 31;
 
-  const int L = blockIdx.x;
-  const int qt = CAUSAL ? (p.n_qt - 1 - L / p.BH) : (L / p.BH);
-  const int bh = L % p.BH;
-  const int b = bh / p.H;
-  const int q0 = qt * BR;
   const int s_q = p.s_q, s_k = p.s_k;
-  // Key range of this workgroup: all keys, or chunk blockIdx.y of a key-split
-  // launch. Key indices below are relative to k0; s_kc keys are in range.
-  const int k0 = SPLIT ? (int)blockIdx.y * p.k_chunk : 0;
-  const int s_kc = SPLIT ? max(0, min(s_k, k0 + p.k_chunk) - k0) : s_k;
-
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (int64_t)bh * s_q * D, (uint32_t)s_q * D * 2);
-  const uint16_t* kg = p.k + ((int64_t)bh * s_k + k0) * D;
-  const uint16_t* vg = p.v + ((int64_t)bh * s_k + k0) * D;
-  const uint8_t* mg = PADMASK ? p.kpm + (int64_t)b * s_k + k0 : nullptr;
-
-  // ---- keys this tile can see: causal stops at the last query row; padding
-  // stops after the last key that is not padded.
-  int kend = s_kc;
-  if (CAUSAL) kend = min(kend, q0 + BR - k0);
-  if (PADMASK) {
-    if (tid == 0) lds_last = -1;
-    __syncthreads();
-    int last = -1;
-    for (int cend = s_kc; cend > 0; cend -= NT * 4) {
-      const int cbeg = max(0, cend - NT * 4);
-      int best = -1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = cbeg + tid * 4 + i;
-        if (j < cend && mg[j] == 0) best = j;
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
-      if (lane == 0 && best >= 0) atomicMax(&lds_last, best);
-      __syncthreads();
-      const int found = lds_last;
-      __syncthreads();
-      if (found >= 0) {
-        last = found;
-        break;
-      }
-    }
-    kend = min(kend, last + 1);
-  }
-  const int n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
+  // ---- work items. Item L is (key chunk, query tile, (b, h)) with the
+  // (b, h) index fastest, so when B*H is a multiple of 8 every item of a head
+  // has the same L mod 8 (the device deals workgroups to its 8 XCDs
+  // round-robin, so a head's items share an XCD's L2); causal launches take
+  // the longest query tiles first. At D = 128 each workgroup takes one item
+  // (L = its index). At D = 64 the grid is persistent (at most one workgroup
+  // per CU), which saves the start and end of a workgroup per item (measured
+  // +8 % on the padded workload; at D = 128 the loop over items made the
+  // compiler's code for the tile loop slower than that saving): workgroup g
+  // takes one item per round, g in even rounds and the mirror image of g
+  // within its round in odd rounds, keeping g mod 8. Mirrored rounds pair
+  // long and short causal tiles, so the workgroups get equal work.
+  constexpr bool PERSIST = !VDMA;
+  const int G = gridDim.x, g = blockIdx.x;
+  auto item_of = [&](int round) -> int {
+    const int off = (round & 1) ? ((G & 7) == 0 ? G - 8 * (1 + g / 8) + (g & 7) : G - 1 - g) : g;
+    return round * G + off;
+  };
+  struct Item {
+    int q0, bh, b, zc, k0, s_kc;
+  };
+  auto describe = [&](int L) -> Item {
+    Item it;
+    const int per_chunk = p.n_qt * p.BH;
+    it.zc = SPLIT ? L / per_chunk : 0;
+    const int Li = SPLIT ? L % per_chunk : L;
+    const int qt = CAUSAL ? (p.n_qt - 1 - Li / p.BH) : (Li / p.BH);
+    it.q0 = qt * BR;
+    it.bh = Li % p.BH;
+    it.b = it.bh / p.H;
+    // key range: all keys, or chunk zc of a key-split launch; key indices
+    // below are relative to k0, s_kc keys are in range
+    it.k0 = SPLIT ? it.zc * p.k_chunk : 0;
+    it.s_kc = SPLIT ? max(0, min(s_k, it.k0 + p.k_chunk) - it.k0) : s_k;
+    return it;
+  };
+  int round = 0;
+  int L_cur = item_of(0);  // < n_items: the grid is at most the item count
+  int boff = 0;            // LDS buffer of cur's tile t: (boff + t) % NBUF
+  int n_kv = 0;            // key tiles cur walks
+  int qlo = 0;             // first query row of this wave in cur
+  const uint16_t* kg = nullptr;  // cur's keys and values from k0 on
+  const uint16_t* vg = nullptr;
+  const uint8_t* mg = nullptr;
+  int k0 = 0, s_kc = 0;
 
   // ---- Q fragments (B operand of the score product), kept in registers.
-  const int qlo = q0 + 32 * wv;  // first query row of this wave
   bf16x8_t qf[DK];
-  {
-    const uint32_t row = (uint32_t)(qlo + ln);
+  auto load_q = [&](const Item& it) {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (int64_t)it.bh * s_q * D, (uint32_t)s_q * D * 2);
+    const uint32_t row = (uint32_t)(it.q0 + 32 * wv + ln);
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8_t, load16(rq, (row * D + 16 * kk + 8 * hl) * 2));
+  };
+  // sign and zero handling of the scale, applied where Q is first used
+  auto fix_q = [&]() {
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
-      u32x4_t x = load16(rq, (row * D + 16 * kk + 8 * hl) * 2);
+      u32x4_t x = __builtin_bit_cast(u32x4_t, qf[kk]);
       x = (x & p.q_and) ^ p.q_xor;
       qf[kk] = __builtin_bit_cast(bf16x8_t, x);
     }
-  }
+  };
 
   // ---- staging of this group's half (keys 32*grp .. 32*grp+31) of a tile
   const int wg = wv & 3;  // wave within its group
@@ -197,11 +204,19 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   }
   // K rows of tile u into LDS; completes asynchronously (the next fenced
   // barrier of this wave waits for it).
+  // Tile u of cur (nothing past its last tile).
+  auto src_tile = [&](const uint16_t* base_cur, int u, const uint16_t*& src, uint32_t& bytes) -> bool {
+    if (u >= n_kv) return false;
+    src = base_cur + (int64_t)u * BC * D;
+    bytes = (uint32_t)max(s_kc - u * BC, 0) * D * 2;
+    return true;
+  };
   auto dma_k = [&](int u) {
-    const int j0 = u * BC;
-    const uint32_t rest = (uint32_t)max(s_kc - j0, 0) * D * 2;
-    const __amdgpu_buffer_rsrc_t rkt = make_rsrc(kg + (int64_t)j0 * D, rest);
-    char* kl = lds + (u % NBUF) * BUF_BYTES + grp * K_SLOTS * 16;
+    const uint16_t* src;
+    uint32_t rest;
+    if (!src_tile(kg, u, src, rest)) return;
+    const __amdgpu_buffer_rsrc_t rkt = make_rsrc(src, rest);
+    char* kl = lds + ((boff + u) & (NBUF - 1)) * BUF_BYTES + grp * K_SLOTS * 16;
 #pragma unroll
     for (int i = 0; i < K_DMA_W; ++i) {
       const int j = wg + 4 * i;
@@ -222,10 +237,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   }
   // V rows of tile u into LDS, the same way as K (VDMA).
   auto dma_v = [&](int u) {
-    const int j0 = u * BC;
-    const uint32_t rest = (uint32_t)max(s_kc - j0, 0) * D * 2;
-    const __amdgpu_buffer_rsrc_t rvt = make_rsrc(vg + (int64_t)j0 * D, rest);
-    char* vl = lds + (u % NBUF) * BUF_BYTES + K_BYTES + grp * V_SLOTS * 16;
+    const uint16_t* src;
+    uint32_t rest;
+    if (!src_tile(vg, u, src, rest)) return;
+    const __amdgpu_buffer_rsrc_t rvt = make_rsrc(src, rest);
+    char* vl = lds + ((boff + u) & (NBUF - 1)) * BUF_BYTES + K_BYTES + grp * V_SLOTS * 16;
 #pragma unroll
     for (int i = 0; i < V_DMA_W; ++i) {
       const int j = ((wg + 3) & 3) + 4 * i;
@@ -233,7 +249,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     }
   };
   // V through registers (not VDMA): load_v(u) fetches this thread's item of
-  // tile u, store_v(u) writes it transposed.
+  // tile u of cur (zeros past its end), store_v(u) writes it transposed.
   u32x4_t vr[V_LD][2];
   auto load_v = [&](int u) {
     const int j0 = u * BC;
@@ -251,7 +267,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     }
   };
   auto store_v = [&](int u) {
-    char* vl = lds + (u % NBUF) * BUF_BYTES + K_BYTES;
+    char* vl = lds + ((boff + u) & (NBUF - 1)) * BUF_BYTES + K_BYTES;
 #pragma unroll
     for (int i = 0; i < V_LD; ++i) {
       const int id = i * GT + gt;
@@ -269,14 +285,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
 
   // ---- per-wave running state: O^T (one query per lane), row max, row sum
   f32x16_t o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t sc[KB];         // scores of the tile between its two steps
   bf16x8_t pf[KB][2];      // weights of the tile between its two steps
   uint32_t mbyte = 1u;     // this lane's padding byte of the tile in flight
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16_t{};
 
   const int k_lane_off = key_of_row(ln) * KS + hl * 16;
   // VDMA: transpose-read offset of V^T: read r (0, 1) of feature block db
@@ -295,17 +307,17 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     // fragment i of tile t's value product: kb = i / 8, ks = (i / 4) & 1, db = i & 3
     const int db = i % DB;
     if constexpr (VDMA) {
-      const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + v_lane_off + (16 * (i / DB)) * RB + db * 64;
+      const char* vl = lds + ((boff + t) & (NBUF - 1)) * BUF_BYTES + K_BYTES + v_lane_off + (16 * (i / DB)) * RB + db * 64;
       const u32x2_t lo = lds_read_tr16(vl);
       const u32x2_t hi = lds_read_tr16(vl + 4 * RB);
       const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
       return __builtin_bit_cast(bf16x8_t, w);
     } else {
-      const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES + v_lane_off;
+      const char* vl = lds + ((boff + t) & (NBUF - 1)) * BUF_BYTES + K_BYTES + v_lane_off;
       return *(const bf16x8_t*)(vl + db * 32 * VS + (i / DB) * 32);
     }
   };
-  // M step, first half: O^T += V_t^T P(t)^T (tile t in LDS buffer t % NBUF).
+  // M step, first half: O^T += V_t^T P(t)^T.
   auto pv = [&](int t) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -325,7 +337,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // chains are interleaved (k-step outer), so consecutive MFMAs never depend
   // on each other's result.
   auto qk = [&](int t) {
-    const char* kl = lds + (t % NBUF) * BUF_BYTES + k_lane_off;
+    const char* kl = lds + ((boff + t) & (NBUF - 1)) * BUF_BYTES + k_lane_off;
     f32x16_t acc[KB];
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
@@ -474,130 +486,183 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     l_run += rs;
   };
 
-  if (n_kv > 0) {
-    dma_k(0);
-    dma_k(1);
-    dma_k(2);
-    if constexpr (VDMA) {
-      dma_v(0);
-      dma_v(1);
-    } else {
-      load_v(0);
-      store_v(0);
-      load_v(1);
-      store_v(1);
-      load_v(2);
+  // ---- the workgroup's items, one after the other
+  for (;;) {
+    const Item cur = describe(L_cur);
+    const int L_next = item_of(round + 1);
+    const bool has_next = PERSIST && L_next < p.n_items;
+    k0 = cur.k0;
+    s_kc = cur.s_kc;
+    kg = p.k + ((int64_t)cur.bh * s_k + k0) * D;
+    vg = p.v + ((int64_t)cur.bh * s_k + k0) * D;
+    mg = PADMASK ? p.kpm + (int64_t)cur.b * s_k + k0 : nullptr;
+    qlo = cur.q0 + 32 * wv;
+    // keys this tile can see: causal stops at the last query row; padding
+    // stops after the last key that is not padded.
+    int kend = s_kc;
+    if (CAUSAL) kend = min(kend, cur.q0 + BR - k0);
+    if (PADMASK) {
+      if (tid == 0) lds_last = -1;
+      __syncthreads();
+      int last = -1;
+      for (int cend = s_kc; cend > 0; cend -= NT * 4) {
+        const int cbeg = max(0, cend - NT * 4);
+        int best = -1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = cbeg + tid * 4 + i;
+          if (j < cend && mg[j] == 0) best = j;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
+        if (lane == 0 && best >= 0) atomicMax(&lds_last, best);
+        __syncthreads();
+        const int found = lds_last;
+        __syncthreads();
+        if (found >= 0) {
+          last = found;
+          break;
+        }
+      }
+      kend = min(kend, last + 1);
     }
-  }
-  __syncthreads();
-
-  // ---- ping-pong schedule: n_kv + 2 intervals, each closed by a workgroup
-  // barrier. M(t) = [PV(t-1), QK(t)] issues matrix-core work, V(t) =
-  // [K (and, VDMA, V) staging, softmax of S(t)] vector-ALU work. Interval 0:
-  // group 0 runs QK(0). Interval t + 1 (t < n_kv): group 0 runs V(t) then
-  // M(t + 1), group 1 runs M(t) then V(t) (M(n_kv) is PV(n_kv - 1) alone).
-  // Interval n_kv + 1: group 1 runs PV(n_kv - 1). Waves w and w + 4 share a
-  // SIMD, so while one is in its M step the other is in its V step and the
-  // two units overlap; within an interval the two waves switch kinds without
-  // a barrier, which saves one barrier per tile over a barrier at every
-  // switch.
-  // LDS buffer u % 4 holds tile u. Its K part is written (by load-to-LDS
-  // in V(u - 3)) in interval u - 2 and read by QK(u) in intervals u (group
-  // 0) and u + 1 (group 1). Its V part is written in interval u - 1 (VDMA:
-  // load-to-LDS in V(u - 2); otherwise stores in M(u - 1), group 0 in
-  // interval u - 1 and group 1 in interval u) and read from the prefetch at
-  // the end of V(u) (interval u + 1) to PV(u) of group 1 (interval u + 2).
-  // So every write comes after the last read of tile u - 4 (K: interval
-  // u - 3, V: interval u - 2), and the fenced barrier closing the interval of
-  // a write waits for it (loads into LDS included) before any read.
-  // The scheduling fences also keep register-only work in its step
-  // (otherwise the compiler sinks the softmax into the next M step to fill
-  // MFMA gaps, and each wave ends up doing both kinds of work serially).
-  auto phase_sync = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
+    n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
+    load_q(cur);
+    if (n_kv > 0) {
+      dma_k(0);
+      dma_k(1);
+      dma_k(2);
+      if constexpr (VDMA) {
+        dma_v(0);
+        dma_v(1);
+      } else {
+        load_v(0);
+        store_v(0);
+        load_v(1);
+        store_v(1);
+        load_v(2);
+      }
+    }
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // End of V(t): the first LA fragments of PV(t) are requested here, so their
-  // latency overlaps the switch to the M step.
-  auto vstep_end = [&](int t) {
-    __builtin_amdgcn_sched_barrier(0);
+    fix_q();
 #pragma unroll
-    for (int i = 0; i < LA; ++i) vpre[i] = v_frag(t, i);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  if (n_kv > 0) {
-    if (grp == 0) {
-      qk(0);
-      phase_sync();
-      for (int t = 0; t < n_kv - 1; ++t) {
-        vstep(t);
-        vstep_end(t);
-        m_step(t, t + 1);
-        phase_sync();
-      }
-      vstep(n_kv - 1);
-      vstep_end(n_kv - 1);
-      pv(n_kv - 1);
-      phase_sync();
-      phase_sync();
-    } else {
-      phase_sync();
-      qk(0);
-      vstep(0);
-      vstep_end(0);
-      phase_sync();
-      for (int t = 1; t < n_kv; ++t) {
-        m_step(t - 1, t);
-        vstep(t);
-        vstep_end(t);
-        phase_sync();
-      }
-      pv(n_kv - 1);
-      phase_sync();
-    }
-  }
+    for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    mbyte = 1u;
 
-  // ---- epilogue: O = O^T / l, lse = m * |scale| + ln(l)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
-  const int row = qlo + ln;
-  if (SPLIT && row < s_q) {
-    // partial result of this key chunk: fp32 O / l and its log-sum-exp
-    const int64_t pr = ((int64_t)blockIdx.y * p.BH + bh) * s_q + row;
-    float* op = p.o_part + pr * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = o[db][4 * g + e] * inv;
-        *(f32x4_t*)(op + 32 * db + 8 * g + 4 * hl) = w;
+    // ---- ping-pong schedule: n_kv + 2 intervals, each closed by a workgroup
+    // barrier. M(t) = [PV(t-1), QK(t)] issues matrix-core work, V(t) =
+    // [K (and, VDMA, V) staging, softmax of S(t)] vector-ALU work. Interval 0:
+    // group 0 runs QK(0). Interval t + 1 (t < n_kv): group 0 runs V(t) then
+    // M(t + 1), group 1 runs M(t) then V(t) (M(n_kv) is PV(n_kv - 1) alone).
+    // Interval n_kv + 1: group 1 runs PV(n_kv - 1). Waves w and w + 4 share a
+    // SIMD, so while one is in its M step the other is in its V step and the
+    // two units overlap; within an interval the two waves switch kinds without
+    // a barrier, which saves one barrier per tile over a barrier at every
+    // switch.
+    // LDS buffer u % 4 holds tile u. Its K part is written (by load-to-LDS
+    // in V(u - 3)) in interval u - 2 and read by QK(u) in intervals u (group
+    // 0) and u + 1 (group 1). Its V part is written in interval u - 1 (VDMA:
+    // load-to-LDS in V(u - 2); otherwise stores in M(u - 1), group 0 in
+    // interval u - 1 and group 1 in interval u) and read from the prefetch at
+    // the end of V(u) (interval u + 1) to PV(u) of group 1 (interval u + 2).
+    // So every write comes after the last read of tile u - 4 (K: interval
+    // u - 3, V: interval u - 2), and the fenced barrier closing the interval of
+    // a write waits for it (loads into LDS included) before any read.
+    // The scheduling fences also keep register-only work in its step
+    // (otherwise the compiler sinks the softmax into the next M step to fill
+    // MFMA gaps, and each wave ends up doing both kinds of work serially).
+    auto phase_sync = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // End of V(t): the first LA fragments of PV(t) are requested here, so their
+    // latency overlaps the switch to the M step.
+    auto vstep_end = [&](int t) {
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int i = 0; i < LA; ++i) vpre[i] = v_frag(t, i);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (n_kv > 0) {
+      if (grp == 0) {
+        qk(0);
+        phase_sync();
+        for (int t = 0; t < n_kv - 1; ++t) {
+          vstep(t);
+          vstep_end(t);
+          m_step(t, t + 1);
+            phase_sync();
+        }
+        vstep(n_kv - 1);
+        vstep_end(n_kv - 1);
+        pv(n_kv - 1);
+        phase_sync();
+        phase_sync();
+      } else {
+        phase_sync();
+        qk(0);
+        vstep(0);
+        vstep_end(0);
+        phase_sync();
+        for (int t = 1; t < n_kv; ++t) {
+          m_step(t - 1, t);
+            vstep(t);
+          vstep_end(t);
+          phase_sync();
+        }
+        pv(n_kv - 1);
+        phase_sync();
       }
     }
-    if (hl == 0) {
-      p.lse_part[pr] = l_tot > 0.f ? m_run * p.scale_abs + __builtin_amdgcn_logf(l_tot) * kLn2
-                                   : -INFINITY;
-    }
-  } else if (row < s_q) {
-    uint16_t* og = p.out + ((int64_t)bh * s_q + row) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2_t w;
-        w[0] = pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
-        w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *(u32x2_t*)(og + 32 * db + 8 * g + 4 * hl) = w;
+
+    // ---- epilogue: O = O^T / l, lse = m * |scale| + ln(l)
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+    const int row = qlo + ln;
+    if (SPLIT && row < s_q) {
+      // partial result of this key chunk: fp32 O / l and its log-sum-exp
+      const int64_t pr = ((int64_t)cur.zc * p.BH + cur.bh) * s_q + row;
+      float* op = p.o_part + pr * D;
+  #pragma unroll
+      for (int db = 0; db < DB; ++db) {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4_t w;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = o[db][4 * g + e] * inv;
+          *(f32x4_t*)(op + 32 * db + 8 * g + 4 * hl) = w;
+        }
+      }
+      if (hl == 0) {
+        p.lse_part[pr] = l_tot > 0.f ? m_run * p.scale_abs + __builtin_amdgcn_logf(l_tot) * kLn2
+                                     : -INFINITY;
+      }
+    } else if (row < s_q) {
+      uint16_t* og = p.out + ((int64_t)cur.bh * s_q + row) * D;
+  #pragma unroll
+      for (int db = 0; db < DB; ++db) {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2_t w;
+          w[0] = pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
+          w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+          *(u32x2_t*)(og + 32 * db + 8 * g + 4 * hl) = w;
+        }
+      }
+      if (hl == 0) {
+        const float lse = l_tot > 0.f
+                              ? m_run * p.scale_abs + __builtin_amdgcn_logf(l_tot) * kLn2
+                              : -INFINITY;
+        p.lse[(int64_t)cur.bh * s_q + row] = lse;
       }
     }
-    if (hl == 0) {
-      const float lse = l_tot > 0.f
-                            ? m_run * p.scale_abs + __builtin_amdgcn_logf(l_tot) * kLn2
-                            : -INFINITY;
-      p.lse[(int64_t)bh * s_q + row] = lse;
-    }
+    if (!has_next) break;
+    boff = (boff + n_kv) & (NBUF - 1);
+    L_cur = L_next;
+    ++round;
   }
 }
 
@@ -609,27 +674,51 @@ constexpr int rows_per_block() {
 
 
 template <int D, bool CAUSAL, bool PADMASK, bool SPLIT>
-hipError_t launch(const FwdParams& p, int grid, int chunks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, PADMASK, SPLIT>), dim3(grid, chunks), dim3(512), 0,
-                     stream, p);
+hipError_t launch(const FwdParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, PADMASK, SPLIT>), dim3(grid), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device): a persistent
+// grid has one workgroup per CU.
+hipError_t cu_count(int* n) {
+  constexpr int kMaxDev = 64;
+  static int cached[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDev && cached[dev] > 0) {
+    *n = cached[dev];
+    return hipSuccess;
+  }
+  int v = 0;
+  e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (v < 1) v = 1;
+  if (dev >= 0 && dev < kMaxDev) cached[dev] = v;
+  *n = v;
+  return hipSuccess;
+}
+
+// Launch over p.n_items work items (set here from the item count).
 template <bool SPLIT>
-hipError_t launch_fwd(const FwdParams& p, int64_t d, bool causal, bool pad, int grid, int chunks,
-                      hipStream_t hs) {
+hipError_t launch_fwd(FwdParams p, int64_t d, bool causal, bool pad, int64_t items, hipStream_t hs) {
+  // one workgroup per item at d = 128, a persistent grid at d = 64
+  int n_cu = 0;
+  if (d == 64) {
+    const hipError_t e = cu_count(&n_cu);
+    if (e != hipSuccess) return e;
+  }
+  p.n_items = (int)items;
+  const int grid = (int)(d == 64 && items > n_cu ? n_cu : items);
   if (d == 128) {
     if (causal)
-      return pad ? launch<128, true, true, SPLIT>(p, grid, chunks, hs)
-                 : launch<128, true, false, SPLIT>(p, grid, chunks, hs);
-    return pad ? launch<128, false, true, SPLIT>(p, grid, chunks, hs)
-               : launch<128, false, false, SPLIT>(p, grid, chunks, hs);
+      return pad ? launch<128, true, true, SPLIT>(p, grid, hs) : launch<128, true, false, SPLIT>(p, grid, hs);
+    return pad ? launch<128, false, true, SPLIT>(p, grid, hs) : launch<128, false, false, SPLIT>(p, grid, hs);
   }
   if (causal)
-    return pad ? launch<64, true, true, SPLIT>(p, grid, chunks, hs)
-               : launch<64, true, false, SPLIT>(p, grid, chunks, hs);
-  return pad ? launch<64, false, true, SPLIT>(p, grid, chunks, hs)
-             : launch<64, false, false, SPLIT>(p, grid, chunks, hs);
+    return pad ? launch<64, true, true, SPLIT>(p, grid, hs) : launch<64, true, false, SPLIT>(p, grid, hs);
+  return pad ? launch<64, false, true, SPLIT>(p, grid, hs) : launch<64, false, false, SPLIT>(p, grid, hs);
 }
 
 // Merge of the key-split partial results (one wave per query row): with
@@ -710,8 +799,8 @@ extern "C" int attn_fwd_validate(const void* q, const void* k, const void* v, co
   if (s_q > kMaxSeq || s_k > kMaxSeq) return ATTN_ERR_SHAPE;
   if (H > 0 && B > INT32_MAX / H) return ATTN_ERR_SHAPE;
   const int64_t BH = B * H;
-  // the grid's work-items must fit 32 bits
-  if (blocks_for(BH, s_q, d) > (int64_t)(UINT32_MAX / 512)) return ATTN_ERR_SHAPE;
+  // the work items (B * H * query tiles) must fit a 32-bit int
+  if (blocks_for(BH, s_q, d) > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
   if (BH == 0 || s_q == 0) return ATTN_OK;
   if (!q || !out || !lse) return ATTN_ERR_NULL;
   if (s_k > 0 && (!k || !v)) return ATTN_ERR_NULL;
@@ -771,7 +860,7 @@ int finish(hipError_t e) {
   return ATTN_OK;
 }
 
-constexpr int64_t kMaxChunks = 65535;  // grid y limit
+constexpr int64_t kMaxChunks = 65535;
 
 // Keys per chunk for n chunks: a multiple of the 64-key tile.
 int64_t chunk_keys(int64_t s_k, int64_t n) {
@@ -791,9 +880,8 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   if (st != ATTN_OK) return st;
   if (B * H == 0 || s_q == 0) return ATTN_OK;
   const FwdParams p = make_params(q, k, v, out, lse, B, H, s_q, s_k, d, scale, key_padding_mask);
-  const int grid = (int)blocks_for(B * H, s_q, d);
   const bool pad = key_padding_mask != nullptr && s_k > 0;
-  return finish(launch_fwd<false>(p, d, causal != 0, pad, grid, 1, (hipStream_t)stream));
+  return finish(launch_fwd<false>(p, d, causal != 0, pad, blocks_for(B * H, s_q, d), (hipStream_t)stream));
 }
 
 extern "C" int64_t attn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t s_q, int64_t d,
@@ -832,15 +920,16 @@ extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void*
   for (int i = 0; i < 6; ++i)
     if (overlaps(workspace, need, bufs[i], sizes[i])) return ATTN_ERR_ALIAS;
   if (((BH * s_q + 3) / 4) > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
+  // work items of the chunked launch: chunks x B * H x query tiles
+  if (blocks_for(BH, s_q, d) * chunks > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
 
   FwdParams p = make_params(q, k, v, out, lse, B, H, s_q, s_k, d, scale, key_padding_mask);
   p.k_chunk = (int)chunk_keys(s_k, chunks);
   p.o_part = (float*)workspace;
   p.lse_part = (float*)((char*)workspace + align256(chunks * BH * s_q * d * 4));
-  const int grid = (int)blocks_for(BH, s_q, d);
   const bool pad = key_padding_mask != nullptr;
   hipStream_t hs = (hipStream_t)stream;
-  st = finish(launch_fwd<true>(p, d, causal != 0, pad, grid, (int)chunks, hs));
+  st = finish(launch_fwd<true>(p, d, causal != 0, pad, blocks_for(BH, s_q, d) * chunks, hs));
   if (st != ATTN_OK) return st;
   const int64_t rows = BH * s_q;
   const int mgrid = (int)((rows + 3) / 4);

@@ -39,6 +39,10 @@ EDGE_CASES = {
     "many_heads_tiny": (15, 4, 8, 33, 33, 64, {}),
     "one_key": (16, 1, 2, 70, 1, 128, {}),
     "long_keys_few_queries": (17, 1, 1, 3, 2500, 128, dict(causal=False)),
+    # d = 64 runs a persistent grid (one workgroup per CU, one item per round):
+    # more items than CUs, a partial last round, heads not a multiple of 8
+    "rounds_causal_d64": (18, 3, 37, 600, 600, 64, dict(causal=True)),
+    "rounds_lengths_d64": (19, 6, 16, 700, 650, 64, dict(mask="lengths")),
 }
 
 
