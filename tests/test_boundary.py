@@ -92,6 +92,8 @@ def call(fn, **over):
     (dict(s_k=-5), E.ATTN_ERR_SHAPE),
     (dict(s_q=(1 << 22) + 1), E.ATTN_ERR_SHAPE),
     (dict(B=1 << 20, H=1 << 12), E.ATTN_ERR_SHAPE),
+    # more work items (B*H*query tiles) than a 32-bit int holds
+    (dict(B=1 << 16, H=1 << 14, s_q=1 << 22), E.ATTN_ERR_SHAPE),
     (dict(d=96), E.ATTN_ERR_HEAD_DIM),
     (dict(d=256), E.ATTN_ERR_HEAD_DIM),
     (dict(q=Q + 8), E.ATTN_ERR_ALIGN),
