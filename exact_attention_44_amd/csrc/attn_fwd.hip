@@ -609,7 +609,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
         phase_sync();
         for (int t = 1; t < n_kv; ++t) {
           m_step(t - 1, t);
-            vstep(t);
+          vstep(t);
           vstep_end(t);
           phase_sync();
         }
