@@ -195,3 +195,32 @@ def test_no_device_allocation_and_side_stream():
     ref = attention_rows_fp64(f64(c, "q"), f64(c, "k"), f64(c, "v"), float(c["scale"]), True, None, picks)[0]
     compare(out.float().cpu().numpy()[0, 3, picks[0][2]].astype(np.float64),
             lse.cpu().numpy()[0, 3, picks[0][2]].astype(np.float64), ref[0], ref[1], "side stream")
+
+
+def test_concurrent_streams():
+    """Launches on two streams that may overlap on the device (the d = 64
+    persistent grid included: each holds at most one workgroup per CU and
+    keeps no state between workgroups) give the same results as alone."""
+    import torch
+
+    from gpu_util import to_device
+    import exact_attention_44_amd as E
+    say("case concurrent streams")
+    cases = [random_case(31, 2, 24, 700, 700, 64, causal=True, mask="lengths"),
+             random_case(32, 2, 24, 600, 650, 64, mask="random"),
+             random_case(33, 1, 16, 520, 520, 128, causal=True)]
+    streams = [torch.cuda.Stream() for _ in cases]
+    base = torch.cuda.current_stream()
+    ins = [to_device(c) for c in cases]
+    outs = []
+    for st in streams:
+        st.wait_stream(base)
+    for (q, k, v, kpm), c, st in zip(ins, cases, streams):
+        with torch.cuda.stream(st):
+            outs.append(E.fwd(q, k, v, causal=bool(c["causal"]), key_padding_mask=kpm,
+                              scale=float(c["scale"])))
+    torch.cuda.synchronize()
+    for (o, l), c, i in zip(outs, cases, range(len(cases))):
+        O_ref, lse_ref = oracle_full(c)
+        compare(o.float().cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64),
+                O_ref, lse_ref, f"stream {i}")
