@@ -59,6 +59,16 @@ MEASURED_TRAFFIC = {
         "source_sha256": "be06a549ac37610a28caed4d470e80b06099ed65f8f649205484d3987cbc0d3a",
         "fetch_bytes": 478420320,
         "write_bytes": 68158443,
+        # SQ counter passes of the same command (mean over the launches after
+        # the first): MFMA-busy cycles per SIMD over SQ busy cycles per shader
+        # engine (32 engines), the clock those busy cycles imply over the
+        # launch, LDS bank conflicts, LDS instructions per wave and 64-key tile
+        "counters": {
+            "mfma_busy_frac": 0.687,
+            "sustained_clock_ghz": 1.64,
+            "lds_bank_conflicts": 0,
+            "lds_instructions_per_wave_tile": 48,
+        },
     },
     "fp8:B=1,H=32,s=8192,d=128,causal": {
         "source_sha256": "1556daab93d21cbc776866bd05d21423775ba4ad366b41b3ae837281fca8d963",
@@ -281,6 +291,8 @@ def main():
             traffic_detail.update(fetch_bytes=measured["fetch_bytes"],
                                   write_bytes=measured["write_bytes"],
                                   source_sha256=current)
+            if "counters" in measured:
+                traffic_detail["counters"] = measured["counters"]
     value = flops * a.steps / wall / 1e12
     achieved = flops / (kern_avg_ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if a.fp8 else PEAK_BF16_TFLOPS
