@@ -40,6 +40,8 @@ CASES = {
     "all_padded": (38, 2, 1, 64, 300, 64, dict(mask="all"), 3),
     "single_tile_runs_plain": (39, 1, 2, 50, 64, 128, {}, 4),
     "negative_scale": (40, 1, 2, 128, 640, 128, dict(scale=-0.09), 5),
+    # d = 64 runs a persistent grid: more (chunk, query tile, head) items than CUs
+    "rounds_d64_causal_lengths": (41, 2, 8, 1000, 3000, 64, dict(causal=True, mask="lengths"), 5),
 }
 
 
