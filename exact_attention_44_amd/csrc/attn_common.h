@@ -23,6 +23,27 @@ typedef int i32x2_t __attribute__((ext_vector_type(2)));
 // hipError_t behind the calling thread's last ATTN_ERR_LAUNCH (any entry point)
 __attribute__((visibility("hidden"))) inline thread_local int g_last_hip_error = 0;
 
+// Compute units of the current device (cached per device; host code): a
+// persistent grid has one workgroup per CU.
+inline hipError_t cu_count(int* n) {
+  constexpr int kMaxDev = 64;
+  static int cached[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDev && cached[dev] > 0) {
+    *n = cached[dev];
+    return hipSuccess;
+  }
+  int v = 0;
+  e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (v < 1) v = 1;
+  if (dev >= 0 && dev < kMaxDev) cached[dev] = v;
+  *n = v;
+  return hipSuccess;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

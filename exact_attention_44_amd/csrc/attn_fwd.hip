@@ -679,27 +679,6 @@ hipError_t launch(const FwdParams& p, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device): a persistent
-// grid has one workgroup per CU.
-hipError_t cu_count(int* n) {
-  constexpr int kMaxDev = 64;
-  static int cached[kMaxDev];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDev && cached[dev] > 0) {
-    *n = cached[dev];
-    return hipSuccess;
-  }
-  int v = 0;
-  e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  if (v < 1) v = 1;
-  if (dev >= 0 && dev < kMaxDev) cached[dev] = v;
-  *n = v;
-  return hipSuccess;
-}
-
 // Launch over p.n_items work items (set here from the item count).
 template <bool SPLIT>
 hipError_t launch_fwd(FwdParams p, int64_t d, bool causal, bool pad, int64_t items, hipStream_t hs) {

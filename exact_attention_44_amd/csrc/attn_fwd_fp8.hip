@@ -58,6 +58,7 @@ struct Fp8Params {
   float* lse;
   const uint8_t* kpm;
   int s_q, s_k, H, BH, n_qt;
+  int n_items;      // work items: query tiles x (b, h)
   float scale;
 };
 
@@ -121,80 +122,29 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   const int hl = lane >> 5;
   const int ln = lane & 31;
 
-  const int L = blockIdx.x;
-  const int qt = CAUSAL ? (p.n_qt - 1 - L / p.BH) : (L / p.BH);
-  const int bh = L % p.BH;
-  const int b = bh / p.H;
-  const int q0 = qt * BR;
   const int s_q = p.s_q, s_k = p.s_k;
-
-  // Per-head score scale: scores enter exp2 as (q8 . k8) * c with
-  // c = |scale * dq * dk| * log2(e); a negative product negates Q (the sign
-  // bit of each code), a zero one zeroes Q.
-  const float dq = p.dsq ? p.dsq[bh] : 1.f;
-  const float dk = p.dsk ? p.dsk[bh] : 1.f;
-  const float dv = p.dsv ? p.dsv[bh] : 1.f;
-  const float cs = p.scale * dq * dk;
-  const float cs_abs = fabsf(cs);
-  const bool zero_scale = cs_abs < 1e-30f;  // NaN propagates
-  const uint32_t q_and = zero_scale ? 0u : ~0u;
-  const uint32_t q_xor = (!zero_scale && cs < 0.f) ? 0x80808080u : 0u;
-  const float c = zero_scale ? kLog2e : cs_abs * kLog2e;
-  const float scale_abs = zero_scale ? 0.f : cs_abs;
-
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (int64_t)bh * s_q * D, (uint32_t)s_q * D);
-  const uint8_t* kg = p.k + (int64_t)bh * s_k * D;
-  const uint8_t* vg = p.v + (int64_t)bh * s_k * D;
-  const uint8_t* mg = PADMASK ? p.kpm + (int64_t)b * s_k : nullptr;
-
-  // ---- keys this tile can see (causal: up to the last query row; padding:
-  // up to the last key that is not padded)
-  int kend = s_k;
-  if (CAUSAL) kend = min(kend, q0 + BR);
-  if (PADMASK) {
-    if (tid == 0) lds_last = -1;
-    __syncthreads();
-    int last = -1;
-    for (int cend = s_k; cend > 0; cend -= NT * 4) {
-      const int cbeg = max(0, cend - NT * 4);
-      int best = -1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = cbeg + tid * 4 + i;
-        if (j < cend && mg[j] == 0) best = j;
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
-      if (lane == 0 && best >= 0) atomicMax(&lds_last, best);
-      __syncthreads();
-      const int found = lds_last;
-      __syncthreads();
-      if (found >= 0) {
-        last = found;
-        break;
-      }
-    }
-    kend = min(kend, last + 1);
-  }
-  const int n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
-
-  // ---- Q (B operand of the score product): lane holds query qlo + ln,
-  // features 64 kk + 32 hl .. +31
-  const int qlo = q0 + 32 * wv;
+  // ---- work items (query tile, (b, h)), (b, h) fastest, the longest causal
+  // tiles first. At D = 128 each workgroup takes one item (L = its index); at
+  // D = 64 the grid is persistent (at most one workgroup per CU) and
+  // workgroup g takes item g in even rounds and its mirror image within the
+  // round (keeping g mod 8) in odd rounds, as the bf16 kernel does.
+  constexpr bool PERSIST = D == 64;
+  const int G = gridDim.x, g = blockIdx.x;
+  auto item_of = [&](int round) -> int {
+    const int off = (round & 1) ? ((G & 7) == 0 ? G - 8 * (1 + g / 8) + (g & 7) : G - 1 - g) : g;
+    return round * G + off;
+  };
+  int round = 0;
+  int L_cur = item_of(0);  // < n_items: the grid is at most the item count
+  int boff = 0;            // LDS buffer of the item's tile t: (boff + t) % NBUF
+  // per-item values (workgroup-uniform)
+  int bh = 0, b = 0, q0 = 0, qlo = 0, n_kv = 0;
+  float dv = 1.f, c = kLog2e, scale_abs = 0.f;
+  uint32_t q_and = ~0u, q_xor = 0u;
+  const uint8_t* kg = nullptr;
+  const uint8_t* vg = nullptr;
+  const uint8_t* mg = nullptr;
   i32x8_t qf[DK];
-  {
-    const uint32_t row = (uint32_t)(qlo + ln);
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4_t x = load16(rq, row * D + 64 * kk + 32 * hl + 16 * u);
-        x = (x & q_and) ^ q_xor;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qf[kk][4 * u + e] = (int)x[e];
-      }
-    }
-  }
 
   // ---- staging of this group's half (keys 32 grp .. 32 grp + 31) of a tile
   const int wg = wv & 3;  // this wave's DMA instruction within its group's half
@@ -213,27 +163,23 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D;
     if (wg < N_DMA)
       load16_to_lds_untracked(kg + (int64_t)j0 * D, rest,
-                              lds + (u % NBUF) * BUF_BYTES + (grp * H_SLOTS + 64 * wg) * 16, k_voff);
+                              lds + ((boff + u) & (NBUF - 1)) * BUF_BYTES + (grp * H_SLOTS + 64 * wg) * 16, k_voff);
   };
   auto dma_v = [&](int u) {
     const int j0 = u * BC;
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D;
     if (wg < N_DMA)
       load16_to_lds_untracked(vg + (int64_t)j0 * D, rest,
-                              lds + (u % NBUF) * BUF_BYTES + K_BYTES + (grp * H_SLOTS + 64 * wg) * 16, v_voff);
+                              lds + ((boff + u) & (NBUF - 1)) * BUF_BYTES + K_BYTES + (grp * H_SLOTS + 64 * wg) * 16, v_voff);
   };
 
   // ---- per-wave running state
   f32x16_t o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t sc[KB];
   float xw[KB][16];        // float32 weights of the tile between its two steps
   i32x8_t pf;              // the same rounded to E4M3 (value product operand)
   uint32_t mbyte = 1u;
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16_t{};
 
   // Score-product fragment reads: lane (ln, hl) reads K row 32 kb + ln at
   // logical slot 4 kk + 2 hl + u (features 64 kk + 32 hl + 16 u ..); the
@@ -260,7 +206,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   }
   auto v_read = [&](int t, int i) -> i32x2_t {
     // read i of tile t's value product: feature block i / 4, byte block i % 4
-    const char* vl = lds + (t % NBUF) * BUF_BYTES + K_BYTES;
+    const char* vl = lds + ((boff + t) & (NBUF - 1)) * BUF_BYTES + K_BYTES;
     const int db = i >> 2, tb = i & 3;
     return lds_read_tr8(vl + v_off[db] + 8 * tb * D);
   };
@@ -279,7 +225,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     for (int i = 0; i < N_VR; ++i) vr[i] = i < LA ? vpre[i < LA ? i : 0] : v_read(t, i);
   };
   auto read_k = [&](int t) {
-    const char* kl = lds + (t % NBUF) * BUF_BYTES;
+    const char* kl = lds + ((boff + t) & (NBUF - 1)) * BUF_BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -428,97 +374,182 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     weights(-((m_run == -INFINITY) ? 0.f : m_run) * c);
   };
 
-  if (n_kv > 0) {
-    dma_k(0);
-    dma_k(1);
-    dma_k(2);
-    dma_v(0);
-    dma_v(1);
-  }
-  wait_loads();
-  __syncthreads();
+  // ---- the workgroup's items, one after the other
+  for (;;) {
+    const int L = L_cur;
+    const int L_next = item_of(round + 1);
+    const bool has_next = PERSIST && L_next < p.n_items;
+    const int qt = CAUSAL ? (p.n_qt - 1 - L / p.BH) : (L / p.BH);
+    bh = L % p.BH;
+    b = bh / p.H;
+    q0 = qt * BR;
+    // Per-head score scale: scores enter exp2 as (q8 . k8) * c with
+    // c = |scale * dq * dk| * log2(e); a negative product negates Q (the sign
+    // bit of each code), a zero one zeroes Q.
+    const float dq = p.dsq ? p.dsq[bh] : 1.f;
+    const float dk = p.dsk ? p.dsk[bh] : 1.f;
+    dv = p.dsv ? p.dsv[bh] : 1.f;
+    const float cs = p.scale * dq * dk;
+    const float cs_abs = fabsf(cs);
+    const bool zero_scale = cs_abs < 1e-30f;  // NaN propagates
+    q_and = zero_scale ? 0u : ~0u;
+    q_xor = (!zero_scale && cs < 0.f) ? 0x80808080u : 0u;
+    c = zero_scale ? kLog2e : cs_abs * kLog2e;
+    scale_abs = zero_scale ? 0.f : cs_abs;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (int64_t)bh * s_q * D, (uint32_t)s_q * D);
+    kg = p.k + (int64_t)bh * s_k * D;
+    vg = p.v + (int64_t)bh * s_k * D;
+    mg = PADMASK ? p.kpm + (int64_t)b * s_k : nullptr;
 
-  // ---- ping-pong schedule, as in the bf16 kernel: n_kv + 2 intervals, each
-  // closed by a workgroup barrier. Interval 0: group 0 runs QK(0). Interval
-  // t + 1 (t < n_kv): group 0 runs V(t) then M(t + 1), group 1 M(t) then V(t)
-  // (M(n_kv) is PV(n_kv - 1) alone). Interval n_kv + 1: group 1 runs
-  // PV(n_kv - 1). LDS buffer u % 4 holds tile u. K(u) is requested by V(u - 3)
-  // in interval u - 2 and read by QK(u) in intervals u (group 0) and u + 1
-  // (group 1); V(u) is requested by V(u - 2) in interval u - 1 and read from
-  // the prefetch at the end of V(u) (interval u + 1) to PV(u) of group 1
-  // (interval u + 2). Every request comes after the last read of tile u - 4
-  // (K: interval u - 3, V: interval u - 2) and is waited for (explicitly: the
-  // requests are untracked) at the barrier closing its interval.
-  auto phase_sync = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
+    // ---- keys this tile can see (causal: up to the last query row; padding:
+    // up to the last key that is not padded)
+    int kend = s_k;
+    if (CAUSAL) kend = min(kend, q0 + BR);
+    if (PADMASK) {
+      if (tid == 0) lds_last = -1;
+      __syncthreads();
+      int last = -1;
+      for (int cend = s_k; cend > 0; cend -= NT * 4) {
+        const int cbeg = max(0, cend - NT * 4);
+        int best = -1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = cbeg + tid * 4 + i;
+          if (j < cend && mg[j] == 0) best = j;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
+        if (lane == 0 && best >= 0) atomicMax(&lds_last, best);
+        __syncthreads();
+        const int found = lds_last;
+        __syncthreads();
+        if (found >= 0) {
+          last = found;
+          break;
+        }
+      }
+      kend = min(kend, last + 1);
+    }
+    n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
+
+    // ---- Q (B operand of the score product): lane holds query qlo + ln,
+    // features 64 kk + 32 hl .. +31
+    qlo = q0 + 32 * wv;
+    {
+      const uint32_t row = (uint32_t)(qlo + ln);
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          u32x4_t x = load16(rq, row * D + 64 * kk + 32 * hl + 16 * u);
+          x = (x & q_and) ^ q_xor;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qf[kk][4 * u + e] = (int)x[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    mbyte = 1u;
+
+    if (n_kv > 0) {
+      dma_k(0);
+      dma_k(1);
+      dma_k(2);
+      dma_v(0);
+      dma_v(1);
+    }
     wait_loads();
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // End of V(t): the first LA reads of PV(t) are issued here, so their
-  // latency overlaps the switch to the M step.
-  auto vstep_end = [&](int t) {
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < LA; ++i) vpre[i] = v_read(t, i);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  if (n_kv > 0) {
-    if (grp == 0) {
-      qk(0);
-      phase_sync();
-      for (int t = 0; t < n_kv - 1; ++t) {
-        vstep(t);
-        vstep_end(t);
-        m_step(t, t + 1);
-        phase_sync();
-      }
-      vstep(n_kv - 1);
-      vstep_end(n_kv - 1);
-      read_v(n_kv - 1);
-      finish();
-      pv_mfma();
-      phase_sync();
-      phase_sync();
-    } else {
-      phase_sync();
-      qk(0);
-      vstep(0);
-      vstep_end(0);
-      phase_sync();
-      for (int t = 1; t < n_kv; ++t) {
-        m_step(t - 1, t);
-        vstep(t);
-        vstep_end(t);
-        phase_sync();
-      }
-      read_v(n_kv - 1);
-      finish();
-      pv_mfma();
-      phase_sync();
-    }
-  }
 
-  // ---- epilogue: O = dv * O^T / l, lse = m |scale dq dk| + ln(l)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? dv * __builtin_amdgcn_rcpf(l_tot) : 0.f;
-  const int row = qlo + ln;
-  if (row < s_q) {
-    uint16_t* og = p.out + ((int64_t)bh * s_q + row) * D;
+    // ---- ping-pong schedule, as in the bf16 kernel: n_kv + 2 intervals, each
+    // closed by a workgroup barrier. Interval 0: group 0 runs QK(0). Interval
+    // t + 1 (t < n_kv): group 0 runs V(t) then M(t + 1), group 1 M(t) then V(t)
+    // (M(n_kv) is PV(n_kv - 1) alone). Interval n_kv + 1: group 1 runs
+    // PV(n_kv - 1). LDS buffer u % 4 holds tile u. K(u) is requested by V(u - 3)
+    // in interval u - 2 and read by QK(u) in intervals u (group 0) and u + 1
+    // (group 1); V(u) is requested by V(u - 2) in interval u - 1 and read from
+    // the prefetch at the end of V(u) (interval u + 1) to PV(u) of group 1
+    // (interval u + 2). Every request comes after the last read of tile u - 4
+    // (K: interval u - 3, V: interval u - 2) and is waited for (explicitly: the
+    // requests are untracked) at the barrier closing its interval.
+    auto phase_sync = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_loads();
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // End of V(t): the first LA reads of PV(t) are issued here, so their
+    // latency overlaps the switch to the M step.
+    auto vstep_end = [&](int t) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2_t w;
-        w[0] = pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
-        w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *(u32x2_t*)(og + 32 * db + 8 * g + 4 * hl) = w;
+      for (int i = 0; i < LA; ++i) vpre[i] = v_read(t, i);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (n_kv > 0) {
+      if (grp == 0) {
+        qk(0);
+        phase_sync();
+        for (int t = 0; t < n_kv - 1; ++t) {
+          vstep(t);
+          vstep_end(t);
+          m_step(t, t + 1);
+          phase_sync();
+        }
+        vstep(n_kv - 1);
+        vstep_end(n_kv - 1);
+        read_v(n_kv - 1);
+        finish();
+        pv_mfma();
+        phase_sync();
+        phase_sync();
+      } else {
+        phase_sync();
+        qk(0);
+        vstep(0);
+        vstep_end(0);
+        phase_sync();
+        for (int t = 1; t < n_kv; ++t) {
+          m_step(t - 1, t);
+          vstep(t);
+          vstep_end(t);
+          phase_sync();
+        }
+        read_v(n_kv - 1);
+        finish();
+        pv_mfma();
+        phase_sync();
       }
     }
-    if (hl == 0) {
-      p.lse[(int64_t)bh * s_q + row] =
-          l_tot > 0.f ? m_run * scale_abs + __builtin_amdgcn_logf(l_tot) * kLn2 : -INFINITY;
+
+    // ---- epilogue: O = dv * O^T / l, lse = m |scale dq dk| + ln(l)
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? dv * __builtin_amdgcn_rcpf(l_tot) : 0.f;
+    const int row = qlo + ln;
+    if (row < s_q) {
+      uint16_t* og = p.out + ((int64_t)bh * s_q + row) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2_t w;
+          w[0] = pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
+          w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+          *(u32x2_t*)(og + 32 * db + 8 * g + 4 * hl) = w;
+        }
+      }
+      if (hl == 0) {
+        p.lse[(int64_t)bh * s_q + row] =
+            l_tot > 0.f ? m_run * scale_abs + __builtin_amdgcn_logf(l_tot) * kLn2 : -INFINITY;
+      }
     }
+    if (!has_next) break;
+    boff = (boff + n_kv) & (NBUF - 1);
+    L_cur = L_next;
+    ++round;
   }
 }
 
@@ -549,7 +580,8 @@ extern "C" int attn_fwd_fp8_validate(const void* q, const void* k, const void* v
   if (s_q > kMaxSeq || s_k > kMaxSeq) return ATTN_ERR_SHAPE;
   if (H > 0 && B > INT32_MAX / H) return ATTN_ERR_SHAPE;
   const int64_t BH = B * H;
-  if (BH * ((s_q + 255) / 256) > (int64_t)(UINT32_MAX / 512)) return ATTN_ERR_SHAPE;
+  // the work items (B * H * query tiles) must fit a 32-bit int
+  if (BH * ((s_q + 255) / 256) > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
   if (BH == 0 || s_q == 0) return ATTN_OK;
   if (!q || !out || !lse) return ATTN_ERR_NULL;
   if (s_k > 0 && (!k || !v)) return ATTN_ERR_NULL;
@@ -592,11 +624,22 @@ extern "C" int attn_fwd_fp8(const void* q, const void* k, const void* v, const f
   p.BH = (int)(B * H);
   p.n_qt = (int)((s_q + 255) / 256);
   p.scale = scale;
-  const int grid = p.BH * p.n_qt;
+  p.n_items = p.BH * p.n_qt;
   const bool pad = key_padding_mask != nullptr && s_k > 0;
   const bool cz = causal != 0;
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e;
+  // one workgroup per item at d = 128, a persistent grid at d = 64
+  int grid = p.n_items;
+  if (d == 64) {
+    int n_cu = 0;
+    e = cu_count(&n_cu);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return ATTN_ERR_LAUNCH;
+    }
+    if (grid > n_cu) grid = n_cu;
+  }
   if (d == 128) {
     e = cz ? (pad ? launch<128, true, true>(p, grid, hs) : launch<128, true, false>(p, grid, hs))
            : (pad ? launch<128, false, true>(p, grid, hs) : launch<128, false, false>(p, grid, hs));

@@ -153,6 +153,10 @@ EDGE_CASES = {
     "one_key": (116, 1, 2, 70, 1, 128, {}),
     "long_keys_few_queries": (117, 1, 1, 3, 2500, 128, {}),
     "long_rows_d128": (118, 1, 2, 256, 4096, 128, dict(causal=True)),
+    # d = 64 runs a persistent grid: more items than CUs, each head with its
+    # own descales, a partial last round
+    "rounds_causal_d64": (119, 3, 37, 600, 600, 64, dict(causal=True)),
+    "rounds_lengths_d64": (120, 6, 16, 700, 650, 64, dict(mask="lengths")),
 }
 
 
