@@ -56,24 +56,24 @@ KERNEL_SOURCE_FP8 = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_f
 # on: reported as null once the source's hash differs.
 MEASURED_TRAFFIC = {
     "B=1,H=32,s=8192,d=128,causal": {
-        "source_sha256": "be06a549ac37610a28caed4d470e80b06099ed65f8f649205484d3987cbc0d3a",
-        "fetch_bytes": 478420320,
-        "write_bytes": 68158443,
+        "source_sha256": "795f1f3fc2006cebf7a5390924e384a6dbb890dfa0571688a80c6d438cbb69b0",
+        "fetch_bytes": 476128097,
+        "write_bytes": 68157440,
         # SQ counter passes of the same command (mean over the launches after
         # the first): MFMA-busy cycles per SIMD over SQ busy cycles per shader
         # engine (32 engines), the clock those busy cycles imply over the
         # launch, LDS bank conflicts, LDS instructions per wave and 64-key tile
         "counters": {
-            "mfma_busy_frac": 0.687,
+            "mfma_busy_frac": 0.688,
             "sustained_clock_ghz": 1.64,
             "lds_bank_conflicts": 0,
             "lds_instructions_per_wave_tile": 48,
         },
     },
     "fp8:B=1,H=32,s=8192,d=128,causal": {
-        "source_sha256": "1556daab93d21cbc776866bd05d21423775ba4ad366b41b3ae837281fca8d963",
-        "fetch_bytes": 202960372,
-        "write_bytes": 68170827,
+        "source_sha256": "41f7a1d48fa19b028cf1c9f357afcc6efe98c8571b89ffbd324ab269a8f08f85",
+        "fetch_bytes": 202755971,
+        "write_bytes": 68176693,
     },
 }
 
