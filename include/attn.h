@@ -37,7 +37,7 @@ typedef enum attn_status {
   ATTN_ERR_ALIGN = 4,    /* q, k, v, out not 16-byte aligned, or lse not 4-byte     */
   ATTN_ERR_ALIAS = 5,    /* out or lse overlaps an input, or out overlaps lse       */
   ATTN_ERR_SCALE = 6,    /* scale is NaN or infinite                                */
-  ATTN_ERR_LAUNCH = 7,   /* the HIP runtime refused the kernel launch               */
+  ATTN_ERR_LAUNCH = 7,   /* the HIP runtime refused the launch or the device query */
   ATTN_ERR_WORKSPACE = 8 /* attn_fwd_split: workspace smaller than required         */
 } attn_status;
 
@@ -69,8 +69,10 @@ typedef enum attn_status {
  * are well inside the float32 range.
  *
  * Ownership and synchrony: the library allocates no device or host memory,
- * keeps no pointer after returning, and holds no state; calls may be made from
- * any thread. The call only enqueues work: results are valid once `stream`
+ * keeps no pointer after returning, and holds no state between calls (at
+ * d = 64 the launch reads the current device's compute-unit count, which it
+ * caches); calls may be made from any thread, and calls on different streams
+ * may overlap. The call only enqueues work: results are valid once `stream`
  * has been synchronised. Faults inside the kernel surface through the HIP
  * runtime at synchronisation, not through this return value.
  *
