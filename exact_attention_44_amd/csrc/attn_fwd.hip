@@ -442,11 +442,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[kb][r] = __builtin_amdgcn_exp2f(x[kb][r]);
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+      // four chains started from the first four weights (0 + w would cost an
+      // add: the compiler may not fold it)
+      float ps[4] = {x[0][0], x[0][1], x[0][2], x[0][3]};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ps[r & 3] += x[kb][r];
+        for (int r = 0; r < 16; ++r)
+          if (kb > 0 || r >= 4) ps[r & 3] += x[kb][r];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll

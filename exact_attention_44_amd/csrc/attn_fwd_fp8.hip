@@ -280,11 +280,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
       for (int r = 0; r < 16; ++r) xw[kb][r] = __builtin_amdgcn_exp2f(xw[kb][r]);
   };
   auto row_sum = [&]() __attribute__((always_inline)) -> float {
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    // four chains started from the first four weights (0 + w would cost an
+    // add: the compiler may not fold it)
+    float ps[4] = {xw[0][0], xw[0][1], xw[0][2], xw[0][3]};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ps[r & 3] += xw[kb][r];
+      for (int r = 0; r < 16; ++r)
+        if (kb > 0 || r >= 4) ps[r & 3] += xw[kb][r];
     return (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
   // Start of an M step: the rest of the softmax of the tile whose scores are
