@@ -56,24 +56,24 @@ KERNEL_SOURCE_FP8 = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_f
 # on: reported as null once the source's hash differs.
 MEASURED_TRAFFIC = {
     "B=1,H=32,s=8192,d=128,causal": {
-        "source_sha256": "795f1f3fc2006cebf7a5390924e384a6dbb890dfa0571688a80c6d438cbb69b0",
-        "fetch_bytes": 476128097,
-        "write_bytes": 68157440,
+        "source_sha256": "a7d8f64b8e2a1b75c1b7f33b6811282ce799a7c3ee0513406f9068b91f819946",
+        "fetch_bytes": 502197043,
+        "write_bytes": 68157909,
         # SQ counter passes of the same command (mean over the launches after
         # the first): MFMA-busy cycles per SIMD over SQ busy cycles per shader
         # engine (32 engines), the clock those busy cycles imply over the
         # launch, LDS bank conflicts, LDS instructions per wave and 64-key tile
         "counters": {
-            "mfma_busy_frac": 0.688,
-            "sustained_clock_ghz": 1.64,
+            "mfma_busy_frac": 0.695,
+            "sustained_clock_ghz": 1.54,
             "lds_bank_conflicts": 0,
             "lds_instructions_per_wave_tile": 48,
         },
     },
     "fp8:B=1,H=32,s=8192,d=128,causal": {
-        "source_sha256": "41f7a1d48fa19b028cf1c9f357afcc6efe98c8571b89ffbd324ab269a8f08f85",
-        "fetch_bytes": 202755971,
-        "write_bytes": 68176693,
+        "source_sha256": "efb8bc8111077fc5686f29e33a9e87e98da2ec2c20568124294c45176e97e9e6",
+        "fetch_bytes": 202776791,
+        "write_bytes": 68177216,
     },
 }
 
