@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace attn_detail {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -24,22 +26,26 @@ typedef int i32x2_t __attribute__((ext_vector_type(2)));
 __attribute__((visibility("hidden"))) inline thread_local int g_last_hip_error = 0;
 
 // Compute units of the current device (cached per device; host code): a
-// persistent grid has one workgroup per CU.
+// persistent grid has one workgroup per CU. Threads calling at once may each
+// query and store the same value; the cache entries are atomic for that.
 inline hipError_t cu_count(int* n) {
   constexpr int kMaxDev = 64;
-  static int cached[kMaxDev];
+  static std::atomic<int> cached[kMaxDev];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDev && cached[dev] > 0) {
-    *n = cached[dev];
-    return hipSuccess;
+  if (dev >= 0 && dev < kMaxDev) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *n = c;
+      return hipSuccess;
+    }
   }
   int v = 0;
   e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   if (v < 1) v = 1;
-  if (dev >= 0 && dev < kMaxDev) cached[dev] = v;
+  if (dev >= 0 && dev < kMaxDev) cached[dev].store(v, std::memory_order_relaxed);
   *n = v;
   return hipSuccess;
 }
