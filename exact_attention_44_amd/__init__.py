@@ -183,13 +183,42 @@ def _check_inputs(q, k, v, key_padding_mask, dtypes=None):
     s_k = k.shape[2]
     if tuple(k.shape) != (B, H, s_k, d) or tuple(v.shape) != (B, H, s_k, d):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
     if key_padding_mask is not None:
         m = key_padding_mask
         if m.dtype not in (torch.uint8, torch.bool) or tuple(m.shape) != (B, s_k):
             raise ValueError("key_padding_mask must be uint8/bool [B, s_k]")
-        if not m.is_cuda or not m.is_contiguous():
-            raise ValueError("key_padding_mask must be a contiguous device tensor")
+        if not m.is_cuda or not m.is_contiguous() or m.device != q.device:
+            raise ValueError("key_padding_mask must be a contiguous tensor on q's device")
     return B, H, s_q, s_k, d
+
+
+def _check_given(t, name, shape, dtype, device):
+    """A caller-supplied output or workspace tensor: the kernels write exactly
+    `shape` elements of `dtype` from its first byte, so anything else is
+    refused before the call."""
+    import torch
+
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)}")
+    if t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    return t
+
+
+def _out_lse(out, lse, B, H, s_q, d, device):
+    import torch
+
+    if out is None:
+        out = torch.empty((B, H, s_q, d), dtype=torch.bfloat16, device=device)
+    else:
+        _check_given(out, "out", (B, H, s_q, d), torch.bfloat16, device)
+    if lse is None:
+        lse = torch.empty((B, H, s_q), dtype=torch.float32, device=device)
+    else:
+        _check_given(lse, "lse", (B, H, s_q), torch.float32, device)
+    return out, lse
 
 
 def fwd(q, k, v, *, causal: bool = False, key_padding_mask=None, scale: Optional[float] = None,
@@ -204,10 +233,7 @@ def fwd(q, k, v, *, causal: bool = False, key_padding_mask=None, scale: Optional
     if scale is None:
         scale = d ** -0.5
     with torch.cuda.device(q.device):
-        if out is None:
-            out = torch.empty((B, H, s_q, d), dtype=torch.bfloat16, device=q.device)
-        if lse is None:
-            lse = torch.empty((B, H, s_q), dtype=torch.float32, device=q.device)
+        out, lse = _out_lse(out, lse, B, H, s_q, d, q.device)
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = attn_fwd(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal, key_padding_mask, stream)
     if st != ATTN_OK:
@@ -232,12 +258,11 @@ def fwd_split(q, k, v, *, n_splits: int, causal: bool = False, key_padding_mask=
     if need < 0:
         raise AttnError(ATTN_ERR_SHAPE)
     with torch.cuda.device(q.device):
-        if out is None:
-            out = torch.empty((B, H, s_q, d), dtype=torch.bfloat16, device=q.device)
-        if lse is None:
-            lse = torch.empty((B, H, s_q), dtype=torch.float32, device=q.device)
+        out, lse = _out_lse(out, lse, B, H, s_q, d, q.device)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is not None and (workspace.device != q.device or not workspace.is_contiguous()):
+            raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = attn_fwd_split(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
@@ -258,21 +283,19 @@ def bwd(q, k, v, out, dout, lse, *, causal: bool = False, key_padding_mask=None,
 
     B, H, s_q, s_k, d = _check_inputs(q, k, v, key_padding_mask)
     for name, t in (("out", out), ("dout", dout)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or tuple(t.shape) != (B, H, s_q, d):
-            raise ValueError(f"{name} must be bfloat16 {(B, H, s_q, d)}")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, s_q) or not lse.is_cuda:
-        raise ValueError(f"lse must be float32 {(B, H, s_q)} on the device")
+        _check_given(t, name, (B, H, s_q, d), torch.bfloat16, q.device)
+    _check_given(lse, "lse", (B, H, s_q), torch.float32, q.device)
     if scale is None:
         scale = d ** -0.5
     with torch.cuda.device(q.device):
-        dq = torch.empty_like(q) if dq is None else dq
-        dk = torch.empty_like(k) if dk is None else dk
-        dv = torch.empty_like(v) if dv is None else dv
+        dq = torch.empty_like(q) if dq is None else _check_given(dq, "dq", q.shape, q.dtype, q.device)
+        dk = torch.empty_like(k) if dk is None else _check_given(dk, "dk", k.shape, k.dtype, q.device)
+        dv = torch.empty_like(v) if dv is None else _check_given(dv, "dv", v.shape, v.dtype, q.device)
         need = attn_bwd_workspace_bytes(B, H, s_q)
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
         ws_bytes = workspace.numel() * workspace.element_size()
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, H, s_q, s_k, d, scale, causal,
@@ -298,15 +321,12 @@ def fwd_fp8(q, k, v, *, descale_q=None, descale_k=None, descale_v=None, causal: 
         if t is None:
             continue
         if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.numel() != B * H
-                or not t.is_cuda or not t.is_contiguous()):
+                or t.device != q.device or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous float32 device tensor of {B * H} elements")
     if scale is None:
         scale = d ** -0.5
     with torch.cuda.device(q.device):
-        if out is None:
-            out = torch.empty((B, H, s_q, d), dtype=torch.bfloat16, device=q.device)
-        if lse is None:
-            lse = torch.empty((B, H, s_q), dtype=torch.float32, device=q.device)
+        out, lse = _out_lse(out, lse, B, H, s_q, d, q.device)
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = attn_fwd_fp8(q, k, v, descale_q, descale_k, descale_v, out, lse, B, H, s_q, s_k, d,
                           scale, causal, key_padding_mask, stream)

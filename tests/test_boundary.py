@@ -147,6 +147,29 @@ def test_fwd_rejects_cpu_tensors(lib):
         E.fwd(q.float(), q, q)
 
 
+def test_given_outputs_are_checked_before_the_call(lib):
+    """Caller-supplied outputs must have exactly the shape, dtype and device the
+    kernels write (host logic of the binding; CPU tensors stand in for device
+    ones, with the CPU as the device)."""
+    torch = pytest.importorskip("torch")
+    cpu = torch.device("cpu")
+    good = torch.empty(2, 3, 5, 64, dtype=torch.bfloat16)
+    assert E._check_given(good, "out", (2, 3, 5, 64), torch.bfloat16, cpu) is good
+    for bad in (torch.empty(2, 3, 4, 64, dtype=torch.bfloat16),      # too few rows
+                torch.empty(2, 3, 5, 64, dtype=torch.float32),       # wrong dtype
+                torch.empty(2, 3, 64, 5, dtype=torch.bfloat16).transpose(2, 3),  # not contiguous
+                None):
+        with pytest.raises(ValueError):
+            E._check_given(bad, "out", (2, 3, 5, 64), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="on"):
+        E._check_given(good, "out", (2, 3, 5, 64), torch.bfloat16, torch.device("meta"))
+    out, lse = E._out_lse(None, None, 2, 3, 5, 64, cpu)
+    assert out.shape == (2, 3, 5, 64) and out.dtype == torch.bfloat16
+    assert lse.shape == (2, 3, 5) and lse.dtype == torch.float32
+    with pytest.raises(ValueError):
+        E._out_lse(out, torch.empty(2, 3, 6), 2, 3, 5, 64, cpu)
+
+
 # ---------------------------------------------------------------- key-split entry point
 WS = 7 << 40  # fake, 256-byte aligned workspace address, overlapping nothing
 

@@ -8,7 +8,7 @@ sampled row is checked exactly as in a full comparison.
 import numpy as np
 import pytest
 
-from gpu_util import compare, f64, run_gpu, say
+from gpu_util import compare, f64, run_gpu, say, to_device
 from oracle import attention_fp64, attention_rows_fp64
 from workloads import WORKLOADS, generate, random_case
 
@@ -224,3 +224,25 @@ def test_concurrent_streams():
         O_ref, lse_ref = oracle_full(c)
         compare(o.float().cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64),
                 O_ref, lse_ref, f"stream {i}")
+
+
+def test_wrappers_refuse_wrong_outputs():
+    """Outputs and workspaces given by the caller are checked before any launch."""
+    import torch
+
+    import exact_attention_44_amd as E
+    c = random_case(20, 1, 2, 100, 100, 64)
+    q, k, v, _ = to_device(c)
+    dev = q.device
+    with pytest.raises(ValueError):
+        E.fwd(q, k, v, out=torch.empty(1, 2, 99, 64, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        E.fwd(q, k, v, lse=torch.empty(1, 2, 100, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        E.fwd_split(q, k, v, n_splits=2, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    out, lse = E.fwd(q, k, v)
+    with pytest.raises(ValueError):
+        E.bwd(q, k, v, out, out, lse, dq=torch.empty(1, 2, 100, 32, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        E.bwd(q, k, v, out, out, lse.cpu())
+    torch.cuda.synchronize()
