@@ -54,7 +54,7 @@ struct BwdParams {
   float* lse2w;        // lse * log2(e), -inf for empty or padding rows, [B*H][s_qp]
   const uint8_t* kpm;
   int s_q, s_k, H, BH, n_qt, n_kt;
-  int s_qp;            // s_q rounded up to 64: workspace rows per (b, h)
+  int s_qp;            // s_q rounded up to 128: workspace rows per (b, h)
   float c;             // scale * log2(e): weights are exp2(q.k c - lse log2(e))
   float scale;
 };
@@ -149,8 +149,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const bool live = lse_row != -INFINITY;  // a row with no visible key has P = 0
   const bool any_dead = __ballot(!live) != 0ull;
   const float lse2 = live ? lse_row * kLog2e : 0.f;
-  // D and lse*log2(e) for the dkv kernel, which loads them 64 rows at a time:
-  // the rows up to the next multiple of 64 are written too (D = 0, lse = -inf,
+  // D and lse*log2(e) for the dkv kernel, which loads them 128 rows at a time:
+  // the rows up to the next multiple of 128 are written too (D = 0, lse = -inf,
   // so they carry no weight)
   if (hl == 0 && row < p.s_qp) {
     const int64_t wi = (int64_t)bh * p.s_qp + row;
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool PADMASK>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdParams p) {
-  constexpr int NT = 256, BK = 128, BQ = 64;
+  constexpr int NT = 256, BK = 128, BQ = 128;
   constexpr int QB = BQ / 32, DK = D / 16, DB = D / 32;
   constexpr int RB = 2 * D;                   // bytes per Q / dO row in LDS
   constexpr int SL = D / 8;                   // 16-byte slots per row
@@ -374,11 +374,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdP
     for (int i = 0; i < NQ; ++i) load16_to_lds(rq, base + 64 * (4 * i + wv) * 16, q_voff[i]);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) load16_to_lds(rd, base + TILE + 64 * (4 * i + wv) * 16, q_voff[i]);
-    // lse*log2e then D of the tile's 64 rows, 16 slots each: wave wv loads
-    // slots 8 (wv & 1) .. +7 of lse*log2e (waves 0, 1) or of D (waves 2, 3).
-    // The workspace holds s_qp >= i0 + 64 rows per (b, h).
+    // lse*log2e then D of the tile's BQ rows, BQ / 4 slots each: wave wv
+    // loads slots LS (wv & 1) .. +LS-1 of lse*log2e (waves 0, 1) or of D
+    // (waves 2, 3). The workspace holds s_qp >= i0 + BQ rows per (b, h).
+    constexpr int LS = BQ / 8;
     const __amdgpu_buffer_rsrc_t rl = make_rsrc((wv < 2 ? l2g : Dg) + i0, BQ * 4);
-    if (lane < 8) load16_to_lds(rl, base + 2 * TILE + 128 * wv, (uint32_t)(16 * (8 * (wv & 1) + lane)));
+    if (lane < LS) load16_to_lds(rl, base + 2 * TILE + 16 * LS * wv, (uint32_t)(16 * (LS * (wv & 1) + lane)));
   };
 
   f32x16_t dkt[DB], dvt[DB];
@@ -580,9 +581,9 @@ bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 
 }  // namespace
 
-// Rows of the workspace per (b, h): s_q rounded up to the dkv kernel's 64-row
+// Rows of the workspace per (b, h): s_q rounded up to the dkv kernel's 128-row
 // query tiles.
-static int64_t ws_rows(int64_t s_q) { return (s_q + 63) / 64 * 64; }
+static int64_t ws_rows(int64_t s_q) { return (s_q + 127) / 128 * 128; }
 
 extern "C" int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t s_q) {
   if (B < 0 || H < 0 || s_q < 0) return -1;

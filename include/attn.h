@@ -183,7 +183,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              void* workspace, int64_t workspace_bytes, void* stream);
 
 /* attn_bwd_workspace_bytes - workspace bytes attn_bwd needs:
- * 2 * B * H * (s_q rounded up to 64) * 4, rounded up to 256 (-1 for negative
+ * 2 * B * H * (s_q rounded up to 128) * 4, rounded up to 256 (-1 for negative
  * sizes). Host-only. */
 int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t s_q);
 

@@ -244,10 +244,11 @@ def call_bwd(**over):
 
 
 def test_bwd_workspace_bytes(lib):
-    # two float32 arrays (D and lse*log2e) of s_q rounded up to 64 rows per (b, h)
+    # two float32 arrays (D and lse*log2e) of s_q rounded up to 128 rows per (b, h)
     assert E.attn_bwd_workspace_bytes(2, 3, 100) == 2 * 6 * 128 * 4
+    assert E.attn_bwd_workspace_bytes(2, 3, 130) == 2 * 6 * 256 * 4
     assert E.attn_bwd_workspace_bytes(1, 32, 8192) == 2 * 32 * 8192 * 4
-    assert E.attn_bwd_workspace_bytes(1, 1, 1) == 512
+    assert E.attn_bwd_workspace_bytes(1, 1, 1) == 1024
     assert E.attn_bwd_workspace_bytes(-1, 3, 100) == -1
 
 
