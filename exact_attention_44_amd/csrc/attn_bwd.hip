@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdP
       // (2) the 32 transpose reads of the gradient operands, then the vector
       //     work (P, dS) that covers their latency;
       // (3) the 16 gradient MFMAs.
-      constexpr int LA = 6;
+      constexpr int LA = D == 128 ? 8 : 6;
       f32x4_t lv[4], dv4[4];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
