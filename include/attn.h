@@ -162,7 +162,7 @@ int64_t attn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t s_q, int64_
  *   workspace        caller-owned device memory, 256-byte aligned, of at
  *                    least attn_bwd_workspace_bytes(B, H, s_q) bytes (it
  *                    holds D = rowsum(dO * O) and lse * log2(e), float32,
- *                    each [B, H, s_q rounded up to 64]); contents on entry
+ *                    each [B, H, s_q rounded up to 128]); contents on entry
  *                    are ignored and on return unspecified
  *   workspace_bytes  its size
  *   stream           a hipStream_t (NULL = the default stream)
