@@ -111,3 +111,39 @@ def test_bwd_deterministic():
     b = E.bwd(q, k, v, out, g, lse, causal=True, key_padding_mask=kpm)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_bwd_no_device_allocation_and_side_stream():
+    """With the caller's gradients and workspace given, the backward pass
+    allocates nothing (no s x s buffer) and runs on whatever stream is
+    current, with the same result as on the default stream."""
+    import torch
+
+    import exact_attention_44_amd as E
+    say("case bwd allocation + side stream")
+    c = random_case(63, 1, 4, 1000, 1000, 128, causal=True)
+    q, k, v, _ = to_device(c)
+    g = torch.from_numpy(dout_for(c, 6).view(np.int16)).view(torch.bfloat16).to(q.device)
+    out, lse = E.fwd(q, k, v, causal=True)
+    ref = E.bwd(q, k, v, out, g, lse, causal=True)
+    torch.cuda.synchronize()
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    ws = torch.empty(E.attn_bwd_workspace_bytes(1, 4, 1000), dtype=torch.uint8, device=q.device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        E.bwd(q, k, v, out, g, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
+    side.synchronize()
+    for t in (dq, dk, dv):
+        t.zero_()
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    torch.cuda.reset_peak_memory_stats()
+    a0 = torch.cuda.memory_allocated()
+    with torch.cuda.stream(side):
+        E.bwd(q, k, v, out, g, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
+    side.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.max_memory_allocated() - a0 == 0
+    assert free0 == free1, (free0, free1)
+    assert all(torch.equal(x, y) for x, y in zip((dq, dk, dv), ref))
