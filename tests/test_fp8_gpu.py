@@ -247,3 +247,41 @@ def test_fp8_headline_workload_sampled_rows():
         assert np.all(err <= bound), (h, float((err / bound).max()))
         assert np.all(np.abs(lse[b, h, r] - l_ref) <= delta[b, h] + LSE_FLOOR)
     say(f"  workload rows: max err/bound={worst:.3f}")
+
+
+def test_fp8_no_device_allocation_and_side_stream():
+    """With out and lse given, the FP8 forward allocates nothing and runs on
+    whatever stream is current, with the same result as on the default stream."""
+    import torch
+
+    import exact_attention_44_amd as E
+    say("case fp8 allocation + side stream")
+    c = fp8_case(124, 1, 4, 600, 600, 128, causal=True)
+    dev = "cuda:0"
+    t = {n: torch.from_numpy(np.ascontiguousarray(c[n + "8"])).to(dev) for n in ("q", "k", "v")}
+    ds = {n: torch.from_numpy(np.ascontiguousarray(c["d" + n])).to(dev) for n in ("q", "k", "v")}
+
+    def call(**kw):
+        return E.fwd_fp8(t["q"], t["k"], t["v"], descale_q=ds["q"], descale_k=ds["k"],
+                         descale_v=ds["v"], causal=True, scale=c["scale"], **kw)
+
+    ref_o, ref_l = call()
+    torch.cuda.synchronize()
+    out, lse = torch.empty_like(ref_o), torch.empty_like(ref_l)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out=out, lse=lse)
+    side.synchronize()
+    out.zero_()
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    torch.cuda.reset_peak_memory_stats()
+    a0 = torch.cuda.memory_allocated()
+    with torch.cuda.stream(side):
+        call(out=out, lse=lse)
+    side.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.max_memory_allocated() - a0 == 0
+    assert free0 == free1, (free0, free1)
+    assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)

@@ -114,3 +114,37 @@ def test_split_deterministic_and_equal_across_calls():
     b = E.fwd_split(q, k, v, n_splits=6, causal=True, key_padding_mask=kpm)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_split_no_device_allocation_and_side_stream():
+    """With out, lse and the workspace given, the key-split forward allocates
+    nothing and runs on whatever stream is current, with the same result as on
+    the default stream."""
+    import torch
+
+    import exact_attention_44_amd as E
+    say("case split allocation + side stream")
+    c = random_case(71, 1, 4, 300, 3000, 128, causal=True)
+    q, k, v, _ = to_device(c)
+    ref_o, ref_l = E.fwd_split(q, k, v, n_splits=5, causal=True)
+    torch.cuda.synchronize()
+    out, lse = torch.empty_like(ref_o), torch.empty_like(ref_l)
+    ws = torch.empty(E.attn_fwd_split_workspace_bytes(1, 4, 300, 128, 5), dtype=torch.uint8,
+                     device=q.device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        E.fwd_split(q, k, v, n_splits=5, causal=True, out=out, lse=lse, workspace=ws)
+    side.synchronize()
+    out.zero_()
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    torch.cuda.reset_peak_memory_stats()
+    a0 = torch.cuda.memory_allocated()
+    with torch.cuda.stream(side):
+        E.fwd_split(q, k, v, n_splits=5, causal=True, out=out, lse=lse, workspace=ws)
+    side.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.max_memory_allocated() - a0 == 0
+    assert free0 == free1, (free0, free1)
+    assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
