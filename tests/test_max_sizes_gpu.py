@@ -1,7 +1,7 @@
 """GPU parity at the longest sequences the entry points accept (2^22 query or
 key positions per (b, h), the limit their host checks enforce).
 
-Two shapes, one long side each:
+Two shapes, one long side each (and the FP8 forward on the long-key one, with 16 queries):
   long keys     200 queries (48 for the backward) against 2^22 keys, d = 64,
                 every key padded with probability 1/2 and the last 4097 keys
                 all padded. The two query tiles walk 65536 key tiles (the
@@ -142,3 +142,16 @@ def test_backward_longest_query_range():
     got = run_bwd_rows(c, g, q_rows, None)
     dq, dk, dv = oracle_bwd(c, g, 2048)
     compare_grads(got, (dq[:, :, q_rows], dk, dv), "long queries")
+
+
+def test_fp8_forward_longest_key_range():
+    """attn_fwd_fp8 with 16 queries against 2^22 keys (d = 64, random padding,
+    the last 4097 keys padded), every row checked against the derived FP8
+    bound (the header of tests/test_fp8_gpu.py)."""
+    from test_fp8_gpu import bound_terms, check, fp8_case, run_gpu8
+
+    c = fp8_case(4424, 1, 1, 16, MAX_SEQ, 64, mask="random")
+    c["kpm"][:, -4097:] = 1
+    say(f"fp8, long keys: s_q=16 s_k={MAX_SEQ} d=64, random padding")
+    O, lse = run_gpu8(c)
+    check(O, lse, *bound_terms(c), "attn_fwd_fp8")
