@@ -16,10 +16,10 @@ from .build import LIB_PATH
 __all__ = [
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
     "ATTN_ERR_ALIAS", "ATTN_ERR_SCALE", "ATTN_ERR_LAUNCH", "ATTN_ERR_WORKSPACE", "AttnError",
-    "load_library", "attn_fwd", "attn_fwd_validate", "attn_fwd_split",
-    "attn_fwd_split_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
-    "attn_last_hip_error", "attn_fwd_fp8", "attn_fwd_fp8_validate", "fwd", "fwd_split", "bwd",
-    "fwd_fp8", "LIB_PATH",
+    "ATTN_SPLIT_SCRATCH_BYTES", "load_library", "attn_fwd", "attn_fwd_validate", "attn_fwd_split",
+    "attn_fwd_split_noalloc", "attn_fwd_split_workspace_bytes", "attn_bwd",
+    "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_fwd_fp8",
+    "attn_fwd_fp8_validate", "fwd", "fwd_split", "fwd_split_noalloc", "bwd", "fwd_fp8", "LIB_PATH",
 ]
 
 ATTN_OK = 0
@@ -31,6 +31,8 @@ ATTN_ERR_ALIAS = 5
 ATTN_ERR_SCALE = 6
 ATTN_ERR_LAUNCH = 7
 ATTN_ERR_WORKSPACE = 8
+# size of the fixed device array attn_fwd_split_noalloc uses (include/attn.h)
+ATTN_SPLIT_SCRATCH_BYTES = 64 << 20
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -70,6 +72,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                    ctypes.c_float, ctypes.c_int, vp, i64, vp, i64, vp]
     lib.attn_fwd_split.restype = ctypes.c_int
+    lib.attn_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                           ctypes.c_float, ctypes.c_int, vp, i64, vp]
+    lib.attn_fwd_split_noalloc.restype = ctypes.c_int
     lib.attn_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
     lib.attn_fwd_split_workspace_bytes.restype = i64
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
@@ -124,6 +129,16 @@ def attn_fwd_split(q, k, v, out, lse, B: int, H: int, s_q: int, s_k: int, d: int
                                          B, H, s_q, s_k, d, float(scale), 1 if causal else 0,
                                          _ptr(key_padding_mask), n_splits, _ptr(workspace),
                                          workspace_bytes, stream)
+
+
+def attn_fwd_split_noalloc(q, k, v, out, lse, B: int, H: int, s_q: int, s_k: int, d: int,
+                           scale: float, causal: bool, key_padding_mask, n_splits: int,
+                           stream) -> int:
+    """The C entry point attn_fwd_split_noalloc with the same arguments."""
+    return load_library().attn_fwd_split_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                                 B, H, s_q, s_k, d, float(scale),
+                                                 1 if causal else 0, _ptr(key_padding_mask),
+                                                 n_splits, stream)
 
 
 def attn_fwd_split_workspace_bytes(B: int, H: int, s_q: int, d: int, n_splits: int) -> int:
@@ -267,6 +282,28 @@ def fwd_split(q, k, v, *, n_splits: int, causal: bool = False, key_padding_mask=
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = attn_fwd_split(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
                             key_padding_mask, int(n_splits), workspace, ws_bytes, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, lse
+
+
+def fwd_split_noalloc(q, k, v, *, n_splits: int, causal: bool = False, key_padding_mask=None,
+                      scale: Optional[float] = None, out=None,
+                      lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """As fwd_split, with the partial results in the library's fixed device
+    array instead of a workspace (attn_fwd_split_noalloc). With `out` and
+    `lse` given, nothing is allocated; calls that overlap on one device race
+    on the array."""
+    import torch
+
+    B, H, s_q, s_k, d = _check_inputs(q, k, v, key_padding_mask)
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(q.device):
+        out, lse = _out_lse(out, lse, B, H, s_q, d, q.device)
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_fwd_split_noalloc(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
+                                    key_padding_mask, int(n_splits), stream)
     if st != ATTN_OK:
         raise AttnError(st)
     return out, lse

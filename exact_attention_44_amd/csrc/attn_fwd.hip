@@ -44,6 +44,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "attn.h"
@@ -876,6 +877,52 @@ extern "C" int64_t attn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t 
   return align256(n_splits * rows * d * 4) + align256(n_splits * rows * 4);
 }
 
+namespace {
+
+// Key-split forward over `chunks` (>= 2) chunks with the partial results in
+// `workspace` (at least attn_fwd_split_workspace_bytes(..., chunks) bytes,
+// 256-byte aligned, checked by the callers): the chunked forward, then the
+// merge, both on `hs`.
+int split_launch(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                 int64_t H, int64_t s_q, int64_t s_k, int64_t d, float scale, int causal,
+                 const uint8_t* key_padding_mask, int64_t chunks, void* workspace, hipStream_t hs) {
+  const int64_t BH = B * H;
+  FwdParams p = make_params(q, k, v, out, lse, B, H, s_q, s_k, d, scale, key_padding_mask);
+  p.k_chunk = (int)chunk_keys(s_k, chunks);
+  p.o_part = (float*)workspace;
+  p.lse_part = (float*)((char*)workspace + align256(chunks * BH * s_q * d * 4));
+  const bool pad = key_padding_mask != nullptr;
+  int st = finish(launch_fwd<true>(p, d, causal != 0, pad, blocks_for(BH, s_q, d) * chunks, hs));
+  if (st != ATTN_OK) return st;
+  const int64_t rows = BH * s_q;
+  const int mgrid = (int)((rows + 3) / 4);
+  if (d == 128)
+    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(mgrid), dim3(256), 0, hs, p.o_part, p.lse_part,
+                       (uint16_t*)out, lse, rows, (int)chunks);
+  else
+    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(mgrid), dim3(256), 0, hs, p.o_part, p.lse_part,
+                       (uint16_t*)out, lse, rows, (int)chunks);
+  return finish(hipGetLastError());
+}
+
+// The chunk count a key-split call uses for n_splits requested chunks: at most
+// one per 64-key tile, and at least one.
+int64_t split_chunks(int64_t s_k, int64_t n_splits) {
+  const int64_t tiles = (s_k + 63) / 64;
+  return n_splits < tiles ? n_splits : (tiles > 0 ? tiles : 1);
+}
+
+// Host checks of a key-split call with `chunks` >= 2 that do not depend on
+// the workspace: grid sizes of the chunked launch and of the merge.
+int split_shape_ok(int64_t BH, int64_t s_q, int64_t d, int64_t chunks) {
+  if (((BH * s_q + 3) / 4) > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
+  // work items of the chunked launch: chunks x B * H x query tiles
+  if (blocks_for(BH, s_q, d) * chunks > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+}  // namespace
+
 extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void* out, float* lse,
                               int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d,
                               float scale, int causal, const uint8_t* key_padding_mask,
@@ -886,8 +933,7 @@ extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void*
   if (st != ATTN_OK) return st;
   if (n_splits < 1 || n_splits > kMaxChunks) return ATTN_ERR_SHAPE;
   // fewer chunks than 64-key tiles would leave chunks empty
-  const int64_t tiles = (s_k + 63) / 64;
-  const int64_t chunks = n_splits < tiles ? n_splits : (tiles > 0 ? tiles : 1);
+  const int64_t chunks = split_chunks(s_k, n_splits);
   if (chunks == 1) return attn_fwd(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
                                    key_padding_mask, stream);
   const int64_t need = attn_fwd_split_workspace_bytes(B, H, s_q, d, chunks);
@@ -901,27 +947,71 @@ extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void*
   const int64_t sizes[6] = {nq, nk, nk, nq, nl, key_padding_mask ? B * s_k : 0};
   for (int i = 0; i < 6; ++i)
     if (overlaps(workspace, need, bufs[i], sizes[i])) return ATTN_ERR_ALIAS;
-  if (((BH * s_q + 3) / 4) > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
-  // work items of the chunked launch: chunks x B * H x query tiles
-  if (blocks_for(BH, s_q, d) * chunks > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
-
-  FwdParams p = make_params(q, k, v, out, lse, B, H, s_q, s_k, d, scale, key_padding_mask);
-  p.k_chunk = (int)chunk_keys(s_k, chunks);
-  p.o_part = (float*)workspace;
-  p.lse_part = (float*)((char*)workspace + align256(chunks * BH * s_q * d * 4));
-  const bool pad = key_padding_mask != nullptr;
-  hipStream_t hs = (hipStream_t)stream;
-  st = finish(launch_fwd<true>(p, d, causal != 0, pad, blocks_for(BH, s_q, d) * chunks, hs));
+  st = split_shape_ok(BH, s_q, d, chunks);
   if (st != ATTN_OK) return st;
-  const int64_t rows = BH * s_q;
-  const int mgrid = (int)((rows + 3) / 4);
-  if (d == 128)
-    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(mgrid), dim3(256), 0, hs, p.o_part, p.lse_part,
-                       (uint16_t*)out, lse, rows, (int)chunks);
-  else
-    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(mgrid), dim3(256), 0, hs, p.o_part, p.lse_part,
-                       (uint16_t*)out, lse, rows, (int)chunks);
-  return finish(hipGetLastError());
+  return split_launch(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal, key_padding_mask,
+                      chunks, workspace, (hipStream_t)stream);
+}
+
+// ---- the key-split forward without a caller workspace: its partial results
+// go to a fixed device array of ATTN_SPLIT_SCRATCH_BYTES bytes (one copy per
+// device, held until the process ends), for callers that cannot allocate.
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address of each device's copy comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is passed
+// to kernels.
+static __device__ __align__(256) char scratch[ATTN_SPLIT_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of the current device's `scratch` (cached per device).
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<void*> cached[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDev) {
+    void* c = cached[dev].load(std::memory_order_acquire);
+    if (c != nullptr) {
+      *out = c;
+      return hipSuccess;
+    }
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (ptr == nullptr) return hipErrorInvalidSymbol;
+  if (dev >= 0 && dev < kMaxDev) cached[dev].store(ptr, std::memory_order_release);
+  *out = ptr;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* out,
+                                      float* lse, int64_t B, int64_t H, int64_t s_q, int64_t s_k,
+                                      int64_t d, float scale, int causal,
+                                      const uint8_t* key_padding_mask, int64_t n_splits,
+                                      void* stream) {
+  int st = attn_fwd_validate(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
+                             key_padding_mask);
+  if (st != ATTN_OK) return st;
+  if (n_splits < 1 || n_splits > kMaxChunks) return ATTN_ERR_SHAPE;
+  const int64_t chunks = split_chunks(s_k, n_splits);
+  if (chunks == 1) return attn_fwd(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
+                                   key_padding_mask, stream);
+  if (B * H == 0 || s_q == 0) return ATTN_OK;
+  // the partial results must fit the fixed array (checked before any HIP call)
+  if (attn_fwd_split_workspace_bytes(B, H, s_q, d, chunks) > (int64_t)ATTN_SPLIT_SCRATCH_BYTES)
+    return ATTN_ERR_WORKSPACE;
+  st = split_shape_ok(B * H, s_q, d, chunks);
+  if (st != ATTN_OK) return st;
+  void* ws = nullptr;
+  st = finish(scratch_address(&ws));
+  if (st != ATTN_OK) return st;
+  return split_launch(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal, key_padding_mask,
+                      chunks, ws, (hipStream_t)stream);
 }
 
 extern "C" const char* attn_status_str(int status) {
@@ -934,7 +1024,7 @@ extern "C" const char* attn_status_str(int status) {
     case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS: out or lse overlaps another buffer";
     case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE: scale is NaN or infinite";
     case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: the HIP runtime refused the launch";
-    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: the workspace is smaller than required";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: the workspace (or the fixed scratch array) is smaller than required";
     default: return "unknown attn status";
   }
 }

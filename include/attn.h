@@ -129,6 +129,40 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* out, float
                    float scale, int causal, const uint8_t* key_padding_mask,
                    int64_t n_splits, void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Size of the fixed device array attn_fwd_split_noalloc keeps its partial
+ * results in (64 MiB; one copy per device). */
+#define ATTN_SPLIT_SCRATCH_BYTES (64ll << 20)
+
+/*
+ * attn_fwd_split_noalloc - attn_fwd_split for callers that cannot allocate
+ * device memory or hold a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the chunks' partial
+ * results go to a fixed device array of ATTN_SPLIT_SCRATCH_BYTES bytes that
+ * the library holds on each device it runs on until the process ends.
+ *
+ * Arguments: as attn_fwd_split without the workspace. The result is that of
+ * attn_fwd_split with the same arguments (the same kernels run).
+ *
+ * Limit: attn_fwd_split_workspace_bytes(B, H, s_q, d, chunks) must not exceed
+ * ATTN_SPLIT_SCRATCH_BYTES, chunks = min(n_splits, ceil(s_k / 64));
+ * larger problems get ATTN_ERR_WORKSPACE before any HIP call (attn_fwd_split
+ * with a workspace serves them). A call that uses one chunk runs attn_fwd and
+ * does not touch the array.
+ *
+ * The library allocates nothing here. On the first call on a device it looks
+ * up that device's copy of the array (hipGetSymbolAddress, with the device
+ * current; ATTN_ERR_LAUNCH if that fails). Every call on a device shares its
+ * array, and nothing in it needs clearing between calls (each call writes all
+ * it reads). Calls that may run at the same time on one device (on different
+ * streams, or from different threads) race on the array and give undefined
+ * results: serialise them, or use attn_fwd_split with separate workspaces.
+ * Other statuses as attn_fwd_split.
+ */
+int attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d,
+                           float scale, int causal, const uint8_t* key_padding_mask,
+                           int64_t n_splits, void* stream);
+
 /*
  * attn_fwd_split_workspace_bytes - workspace bytes attn_fwd_split needs for
  * `n_splits` chunks (0 when n_splits == 1); -1 for invalid sizes (negative

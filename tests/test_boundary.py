@@ -35,7 +35,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = header_functions()
     assert names == ["attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_fp8",
-                     "attn_fwd_fp8_validate", "attn_fwd_split", "attn_fwd_split_workspace_bytes",
+                     "attn_fwd_fp8_validate", "attn_fwd_split", "attn_fwd_split_noalloc",
+                     "attn_fwd_split_workspace_bytes",
                      "attn_fwd_validate", "attn_last_hip_error", "attn_status_str"]
     for n in names:
         assert hasattr(lib, n), n
@@ -227,6 +228,52 @@ def test_split_empty_problems_are_no_ops(lib):
     null = dict(q=None, k=None, v=None, out=None, lse=None)
     assert call_split(B=0, **null) == E.ATTN_OK
     assert call_split(s_q=0, **null) == E.ATTN_OK
+
+
+def call_split_noalloc(n_splits=4, **over):
+    a = dict(GOOD, **over)
+    args = [a[n] for n in ("q", "k", "v", "out", "lse", "B", "H", "s_q", "s_k", "d", "scale",
+                           "causal", "key_padding_mask")]
+    return E.attn_fwd_split_noalloc(*args, n_splits, None)
+
+
+def test_split_noalloc_scratch_size_matches_header(lib):
+    src = open(HEADER).read()
+    m = re.search(r"#define ATTN_SPLIT_SCRATCH_BYTES \((\d+)ll << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == E.ATTN_SPLIT_SCRATCH_BYTES == 64 << 20
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_splits=0), E.ATTN_ERR_SHAPE),
+    (dict(n_splits=65536), E.ATTN_ERR_SHAPE),
+    (dict(q=None), E.ATTN_ERR_NULL),
+    (dict(d=96), E.ATTN_ERR_HEAD_DIM),
+    (dict(scale=float("inf")), E.ATTN_ERR_SCALE),
+    (dict(out=Q + 64), E.ATTN_ERR_ALIAS),
+    # partial results beyond the fixed array: 2 chunks x 32 heads x 2048 rows
+    # x (128 + 1) floats = 67.6 MB > 64 MiB
+    (dict(B=1, H=32, s_q=2048, s_k=4096, n_splits=2), E.ATTN_ERR_WORKSPACE),
+    (dict(B=1, H=1, s_q=1 << 22, s_k=4096, d=64, n_splits=64), E.ATTN_ERR_WORKSPACE),
+])
+def test_split_noalloc_rejected_before_launch(lib, kw, code):
+    over = {k: v for k, v in kw.items() if k in GOOD}
+    rest = {k: v for k, v in kw.items() if k not in GOOD}
+    assert call_split_noalloc(**rest, **over) == code
+
+
+def test_split_noalloc_limit_is_the_workspace_size(lib):
+    # the largest row count whose two-chunk partials fit 64 MiB at d = 128
+    rows_fit = (64 << 20) // (2 * 129 * 4) // 256 * 256
+    assert ws_bytes(1, 1, rows_fit, 128, 2) <= 64 << 20
+    assert ws_bytes(1, 1, rows_fit + 4096, 128, 2) > 64 << 20
+    assert call_split_noalloc(B=1, H=1, s_q=rows_fit + 4096, s_k=4096, n_splits=2,
+                              key_padding_mask=None) == E.ATTN_ERR_WORKSPACE
+
+
+def test_split_noalloc_empty_problems_are_no_ops(lib):
+    null = dict(q=None, k=None, v=None, out=None, lse=None)
+    assert call_split_noalloc(B=0, **null) == E.ATTN_OK
+    assert call_split_noalloc(s_q=0, **null) == E.ATTN_OK
 
 
 # ---------------------------------------------------------------- backward entry point
