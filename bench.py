@@ -26,7 +26,13 @@ of known size after the timed region, so a counter profile of this command also
 holds the reference that scales FETCH_SIZE / WRITE_SIZE to bytes; --fp8
 times the 8-bit-float forward (attn_fwd_fp8) on the same workload, its inputs
 quantised per (batch item, head) to OCP E4M3 codes with float32 descale
-factors, against the dense FP8 MFMA peak.
+factors, against the dense FP8 MFMA peak; --unfused times the materialising
+path (attn_fwd_unfused: score matrix written to device memory, softmax in
+place, value product) on the workload, with the fused forward timed beside it
+for the ratio, against the HBM bandwidth peak. The default line also carries
+the kernel's roofline fraction on the s = 4096 and s = 32768 causal workloads
+and on the padded d = 64 one (`other_workloads`; --no-other-workloads skips
+them, as the profiler commands do).
 """
 import argparse
 import json
@@ -44,6 +50,8 @@ METRIC = "attention fwd TFLOP/s at 1 MI355X (s=4096–32768) + % of bf16 MFMA pe
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 # MI355X dense FP8 MFMA: twice the bf16 rate
 PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
+# MI355X HBM3E bandwidth
+PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 1 << 30
 KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_fwd.hip")
 KERNEL_SOURCE_FP8 = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_fwd_fp8.hip")
@@ -97,6 +105,11 @@ def parse():
     ap.add_argument("--fp8", action="store_true",
                     help="time the 8-bit-float forward (attn_fwd_fp8) on E4M3-quantised "
                          "inputs of the workload instead")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the materialising forward (attn_fwd_unfused) on the workload "
+                         "instead, and the fused forward beside it for the ratio")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the short timings of the other forward workloads")
     ap.add_argument("--splits", type=int, default=4,
                     help="key chunks for --split-workload (1 = the plain launch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -104,6 +117,74 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true")
     return ap.parse_args()
+
+
+def cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def time_launches(step, stream, n, ramp_ms=50.0):
+    """Average and minimum duration (ms) of n launches of `step`, each between
+    two HIP events on `stream`, after ramp_ms of untimed launches."""
+    import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ramp_ms:
+        step()
+        torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    return sum(ms) / len(ms), min(ms)
+
+
+def other_workloads(E, dev, stream, skip_name):
+    """Kernel roofline fractions of attn_fwd on the other forward workloads of
+    the metric's range (s = 4096 and s = 32768 causal) and on the padded
+    d = 64 one: seeded inputs, 30 launches each timed with HIP events."""
+    import numpy as np
+    import torch
+
+    from workloads import WORKLOADS, generate
+    res = {}
+    for w in WORKLOADS[1:]:
+        if w.name == skip_name:
+            continue
+        g = generate(w)
+        q, k, v = (torch.from_numpy(g[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
+        del g["q"], g["k"], g["v"]
+        kpm = None if g["kpm"] is None else torch.from_numpy(g["kpm"]).to(dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.s_q), dtype=torch.float32, device=dev)
+        args = (q, k, v, out, lse, w.B, w.H, w.s_q, w.s_k, w.d, float(g["scale"]), w.causal, kpm,
+                stream.cuda_stream)
+
+        def step():
+            st = E.attn_fwd(*args)
+            if st != E.ATTN_OK:
+                raise E.AttnError(st)
+        avg, mn = time_launches(step, stream, 30)
+        r = {"kernel_avg_ms": round(avg, 5), "kernel_min_ms": round(mn, 5),
+             "achieved_tflops": round(w.flops() / (avg * 1e-3) / 1e12, 2),
+             "frac": round(w.flops() / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        if w.padded:
+            useful = sum(4.0 * w.H * w.s_q * int(n) * w.d for n in g["lengths"])
+            r["useful_frac"] = round(useful / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        res[w.name] = r
+        del q, k, v, out, lse, kpm
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, g, target_s, backward=False, fp8=None):
@@ -153,11 +234,14 @@ def cpu_baseline(w, g, target_s, backward=False, fp8=None):
         "value": round(per_head * heads / spent / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
+        "host_cpu_count": os.cpu_count(),
+        "cpu_model": cpu_model(),
+        "openblas_num_threads": os.environ.get("OPENBLAS_NUM_THREADS"),
         "kind": "oracle",
         "sample": (f"float64 NumPy oracle{' gradients' if backward else ''}"
                    f"{' on E4M3 inputs' if fp8 is not None else ''} (materialises each head's s x s scores, row blocks "
                    f"of 2048) on {heads} of {w.B * w.H} heads of {w.name}: {spent:.1f} s on "
-                   f"{threads} BLAS threads, {platform.processor() or platform.machine()}; "
+                   f"{threads} BLAS threads of {os.cpu_count()} host CPUs ({cpu_model()}); "
                    f"FLOPs counted with the metric formula"),
     }
 
@@ -224,6 +308,14 @@ def main():
                             float(g["scale"]), w.causal, kpm, bws, bws.numel(), stream.cuda_stream)
             if st != E.ATTN_OK:
                 raise E.AttnError(st)
+    elif a.unfused:
+        s_bytes = E.attn_fwd_unfused_workspace_bytes(w.B, w.H, w.s_q, w.s_k)
+        scores = torch.empty(max(s_bytes, 16), dtype=torch.uint8, device=dev)  # outside the timed region
+
+        def step():
+            st = E.attn_fwd_unfused(*args[:13], scores, s_bytes, args[13])
+            if st != E.ATTN_OK:
+                raise E.AttnError(st)
     elif split:
         chunks = max(1, min(a.splits, (w.s_k + 63) // 64))
         ws_bytes = E.attn_fwd_split_workspace_bytes(w.B, w.H, w.s_q, w.d, chunks)
@@ -269,8 +361,19 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    fused_ms = None
+    if a.unfused:
+        def fused_step():
+            st = E.attn_fwd(*args)
+            if st != E.ATTN_OK:
+                raise E.AttnError(st)
+        fused_ms = time_launches(fused_step, stream, a.steps)[0]
+
     flops = w.flops() * (2.5 if a.backward else 1.0)
-    if a.fp8:  # E4M3 q, k, v (one byte each) and the descales read; bf16 out, lse written
+    if a.unfused:  # the score matrix written, read and written in place, read again
+        algorithmic_bytes = 8 * w.B * w.H * w.s_q * w.s_k + 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d \
+            + 2 * w.B * w.H * w.s_q * w.d + 4 * w.B * w.H * w.s_q
+    elif a.fp8:  # E4M3 q, k, v (one byte each) and the descales read; bf16 out, lse written
         algorithmic_bytes = w.B * w.H * (w.s_q + 2 * w.s_k) * w.d + 12 * w.B * w.H \
             + 2 * w.B * w.H * w.s_q * w.d + 4 * w.B * w.H * w.s_q
     elif a.backward:  # read q, out, dout, k, v, lse; write dq, dk, dv
@@ -280,7 +383,7 @@ def main():
         algorithmic_bytes = 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d + 2 * w.B * w.H * w.s_q * w.d \
             + 4 * w.B * w.H * w.s_q
     traffic, traffic_detail = None, {"algorithmic_bytes": algorithmic_bytes}
-    measured = None if (a.backward or split) else \
+    measured = None if (a.backward or split or a.unfused) else \
         MEASURED_TRAFFIC.get(("fp8:" if a.fp8 else "") + w.name)
     if measured is not None:
         import hashlib
@@ -338,6 +441,21 @@ def main():
         res["dtype"] = "fp8-e4m3 products, fp32 accumulate, bf16 out"
         res["pct_of_fp8_peak"] = round(100.0 * value / PEAK_FP8_TFLOPS, 2)
         del res["pct_of_bf16_peak"]
+    if a.unfused:
+        gbs = algorithmic_bytes / (kern_avg_ms * 1e-3) / 1e9
+        res["metric"] = METRIC.replace(" + % of bf16 MFMA peak", "") + " (unfused materialising path)"
+        res["config"]["entry_point"] = "attn_fwd_unfused"
+        res["roofline"].update(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                               frac=round(gbs / PEAK_HBM_GBS, 4),
+                               kernel="unf_scores_kernel + unf_softmax_kernel + unf_values_kernel "
+                                      "(the three kernels of one call, timed together)")
+        res["unfused"] = {
+            "score_matrix_bytes": s_bytes,
+            "score_matrix_gb": round(s_bytes / 1e9, 2),
+            "fused_kernel_avg_ms": round(fused_ms, 5),
+            "unfused_over_fused_time": round(kern_avg_ms / fused_ms, 3),
+        }
+        del res["pct_of_bf16_peak"]
     if a.backward:
         res["config"]["pass"] = "backward"
         res["metric"] = METRIC + " (backward pass: dq, dk, dv)"
@@ -347,8 +465,11 @@ def main():
     if w.padded:
         # the metric's nominal FLOPs ignore padding; the work on visible keys only
         lengths = g["lengths"]
-        useful = sum(4.0 * w.H * w.s_q * int(n) * w.d for n in lengths)
+        useful = sum(4.0 * w.H * w.s_q * int(n) * w.d for n in lengths) * (2.5 if a.backward else 1.0)
         res["useful_tflops"] = round(useful * a.steps / wall / 1e12, 2)
+    plain = not (a.fp8 or a.backward or split or a.unfused)
+    if plain and not a.no_other_workloads:
+        res["other_workloads"] = other_workloads(E, dev, stream, w.name)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, g, a.cpu_seconds, backward=a.backward, fp8=fp8)
     print(json.dumps(res), flush=True)

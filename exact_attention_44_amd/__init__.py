@@ -19,7 +19,8 @@ __all__ = [
     "ATTN_SPLIT_SCRATCH_BYTES", "load_library", "attn_fwd", "attn_fwd_validate", "attn_fwd_split",
     "attn_fwd_split_noalloc", "attn_fwd_split_workspace_bytes", "attn_bwd",
     "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_fwd_fp8",
-    "attn_fwd_fp8_validate", "fwd", "fwd_split", "fwd_split_noalloc", "bwd", "fwd_fp8", "LIB_PATH",
+    "attn_fwd_fp8_validate", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes", "fwd",
+    "fwd_split", "fwd_split_noalloc", "bwd", "fwd_fp8", "fwd_unfused", "LIB_PATH",
 ]
 
 ATTN_OK = 0
@@ -88,6 +89,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_fp8_validate.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                           i64, ctypes.c_float, ctypes.c_int, vp]
     lib.attn_fwd_fp8_validate.restype = ctypes.c_int
+    lib.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                     ctypes.c_float, ctypes.c_int, vp, vp, i64, vp]
+    lib.attn_fwd_unfused.restype = ctypes.c_int
+    lib.attn_fwd_unfused_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.attn_fwd_unfused_workspace_bytes.restype = i64
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -175,6 +181,19 @@ def attn_fwd_fp8_validate(q, k, v, descale_q, descale_k, descale_v, out, lse, B:
                                                 _ptr(descale_k), _ptr(descale_v), _ptr(out),
                                                 _ptr(lse), B, H, s_q, s_k, d, float(scale),
                                                 1 if causal else 0, _ptr(key_padding_mask))
+
+
+def attn_fwd_unfused(q, k, v, out, lse, B: int, H: int, s_q: int, s_k: int, d: int, scale: float,
+                     causal: bool, key_padding_mask, scores, scores_bytes: int, stream) -> int:
+    """The C entry point attn_fwd_unfused with the same arguments."""
+    return load_library().attn_fwd_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                           B, H, s_q, s_k, d, float(scale), 1 if causal else 0,
+                                           _ptr(key_padding_mask), _ptr(scores), scores_bytes,
+                                           stream)
+
+
+def attn_fwd_unfused_workspace_bytes(B: int, H: int, s_q: int, s_k: int) -> int:
+    return load_library().attn_fwd_unfused_workspace_bytes(B, H, s_q, s_k)
 
 
 def attn_status_str(status: int) -> str:
@@ -370,3 +389,31 @@ def fwd_fp8(q, k, v, *, descale_q=None, descale_k=None, descale_v=None, causal: 
     if st != ATTN_OK:
         raise AttnError(st)
     return out, lse
+
+
+def fwd_unfused(q, k, v, *, causal: bool = False, key_padding_mask=None,
+                scale: Optional[float] = None, out=None, lse=None, scores=None):
+    """The materialising forward (attn_fwd_unfused) on torch device tensors, as
+    fwd. `scores` is an optional bf16 [B, H, s_q, s_k] device tensor for the
+    score matrix (allocated with torch when None); on return it holds the
+    softmax weights. Returns (out, lse, scores)."""
+    import torch
+
+    B, H, s_q, s_k, d = _check_inputs(q, k, v, key_padding_mask)
+    if scale is None:
+        scale = d ** -0.5
+    need = attn_fwd_unfused_workspace_bytes(B, H, s_q, s_k)
+    if need < 0:
+        raise AttnError(ATTN_ERR_SHAPE)
+    with torch.cuda.device(q.device):
+        out, lse = _out_lse(out, lse, B, H, s_q, d, q.device)
+        if scores is None:
+            scores = torch.empty((B, H, s_q, s_k), dtype=torch.bfloat16, device=q.device)
+        else:
+            _check_given(scores, "scores", (B, H, s_q, s_k), torch.bfloat16, q.device)
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_fwd_unfused(q, k, v, out, lse, B, H, s_q, s_k, d, scale, causal,
+                              key_padding_mask, scores if need > 0 else None, need, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, lse, scores

@@ -7,7 +7,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", n) for n in ("attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_unfused.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libattn.so")
 

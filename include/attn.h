@@ -265,6 +265,50 @@ int attn_fwd_fp8_validate(const void* q, const void* k, const void* v, const flo
                           const float* lse, int64_t B, int64_t H, int64_t s_q, int64_t s_k,
                           int64_t d, float scale, int causal, const uint8_t* key_padding_mask);
 
+/*
+ * attn_fwd_unfused - the same operation as attn_fwd, computed the
+ * materialising way the fused kernel avoids: the score matrix of every
+ * (batch item, head) is written to device memory, turned into weights in
+ * place, and multiplied by the values. It exists to measure that path.
+ *
+ * The onecalc.app page "Attention memory" sizes the matrix ("The formula",
+ * "Worked example"): B * H * s_q * s_k elements of e = 2 bytes (16-bit
+ * scores), 1.07 GB at B = 1, H = 32, s = 4096 and 4.29 GB at s = 8192. The
+ * hyper.ai story on PyTorch's attention backends reports the plain backend
+ * that stores it as several times slower than the fused ones.
+ *
+ * Three kernels run in order on `stream`:
+ *   1. scores[b,h,i,j] = bf16(scale * q[b,h,i,:].k[b,h,j,:]) (no masks);
+ *   2. in place, per row: hidden keys (causal j > i, padded keys) get weight
+ *      0, the others softmax of the stored scores, rounded to bf16;
+ *      lse[b,h,i] = max + ln(sum exp(s - max)) over the visible stored scores
+ *      (-inf and an all-zero row when no key is visible);
+ *   3. out[b,h,i,:] = bf16(sum_j scores[b,h,i,j] * v[b,h,j,:]) (float32 sums).
+ * The rounding of the scores to bf16 makes the result differ from attn_fwd's
+ * by more than rounding of the output: each weight may move by a factor up
+ * to exp(+-2^-7 max|score|).
+ *
+ * Arguments: as attn_fwd, plus
+ *   scores        caller-owned device memory, 16-byte aligned, of at least
+ *                 attn_fwd_unfused_workspace_bytes(B, H, s_q, s_k) bytes; on
+ *                 return it holds the weights, bf16 [B, H, s_q, s_k]
+ *                 (row-major); may be NULL when that size is 0
+ *   scores_bytes  its size
+ * Statuses as attn_fwd, and ATTN_ERR_NULL / ATTN_ERR_ALIGN /
+ * ATTN_ERR_WORKSPACE / ATTN_ERR_ALIAS for a missing, misaligned, short or
+ * overlapping scores buffer, ATTN_ERR_SHAPE when its size overflows 64 bits
+ * or a grid does not fit. The library allocates nothing.
+ */
+int attn_fwd_unfused(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t B, int64_t H, int64_t s_q, int64_t s_k, int64_t d, float scale,
+                     int causal, const uint8_t* key_padding_mask, void* scores,
+                     int64_t scores_bytes, void* stream);
+
+/* attn_fwd_unfused_workspace_bytes - bytes of the score matrix attn_fwd_unfused
+ * needs: B * H * s_q * s_k * 2 (0 when any size is 0; -1 for negative sizes
+ * or a product beyond 64 bits). Host-only. */
+int64_t attn_fwd_unfused_workspace_bytes(int64_t B, int64_t H, int64_t s_q, int64_t s_k);
+
 /* attn_status_str - a static, human-readable name for a status code. */
 const char* attn_status_str(int status);
 

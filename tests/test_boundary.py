@@ -36,7 +36,8 @@ def test_exports_every_declared_function(lib):
     names = header_functions()
     assert names == ["attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_fp8",
                      "attn_fwd_fp8_validate", "attn_fwd_split", "attn_fwd_split_noalloc",
-                     "attn_fwd_split_workspace_bytes",
+                     "attn_fwd_split_workspace_bytes", "attn_fwd_unfused",
+                     "attn_fwd_unfused_workspace_bytes",
                      "attn_fwd_validate", "attn_last_hip_error", "attn_status_str"]
     for n in names:
         assert hasattr(lib, n), n
@@ -274,6 +275,53 @@ def test_split_noalloc_empty_problems_are_no_ops(lib):
     null = dict(q=None, k=None, v=None, out=None, lse=None)
     assert call_split_noalloc(B=0, **null) == E.ATTN_OK
     assert call_split_noalloc(s_q=0, **null) == E.ATTN_OK
+
+
+# ---------------------------------------------------------------- unfused entry point
+SC = 13 << 40  # fake, 16-byte aligned score-matrix address, overlapping nothing
+
+
+def call_unfused(scores=SC, scores_bytes=None, **over):
+    a = dict(GOOD, **over)
+    if scores_bytes is None:
+        scores_bytes = a["B"] * a["H"] * a["s_q"] * a["s_k"] * 2
+    args = [a[n] for n in ("q", "k", "v", "out", "lse", "B", "H", "s_q", "s_k", "d", "scale",
+                           "causal", "key_padding_mask")]
+    return E.attn_fwd_unfused(*args, scores, scores_bytes, None)
+
+
+def test_unfused_workspace_is_the_score_matrix(lib):
+    from oracle import score_matrix_bytes
+    for B, H, s in ((1, 32, 4096), (1, 32, 8192), (4, 16, 2048), (1, 1, 1)):
+        assert E.attn_fwd_unfused_workspace_bytes(B, H, s, s) == score_matrix_bytes(B, H, s, 2)
+    assert E.attn_fwd_unfused_workspace_bytes(2, 3, 100, 90) == 2 * 3 * 100 * 90 * 2
+    assert E.attn_fwd_unfused_workspace_bytes(2, 3, 0, 90) == 0
+    assert E.attn_fwd_unfused_workspace_bytes(2, 3, 100, 0) == 0
+    assert E.attn_fwd_unfused_workspace_bytes(-1, 3, 100, 90) == -1
+    assert E.attn_fwd_unfused_workspace_bytes(1 << 30, 1 << 30, 1 << 22, 1 << 22) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(scores=None), E.ATTN_ERR_NULL),
+    (dict(scores=SC + 8), E.ATTN_ERR_ALIGN),
+    (dict(scores_bytes=2 * 3 * 100 * 90 * 2 - 1), E.ATTN_ERR_WORKSPACE),
+    (dict(scores=Q + 4096), E.ATTN_ERR_ALIAS),
+    (dict(scores=LSE - 64), E.ATTN_ERR_ALIAS),
+    (dict(q=None), E.ATTN_ERR_NULL),
+    (dict(d=96), E.ATTN_ERR_HEAD_DIM),
+    (dict(scale=float("nan")), E.ATTN_ERR_SCALE),
+    (dict(B=-1), E.ATTN_ERR_SHAPE),
+])
+def test_unfused_rejected_before_launch(lib, kw, code):
+    over = {k: v for k, v in kw.items() if k in GOOD}
+    rest = {k: v for k, v in kw.items() if k not in GOOD}
+    assert call_unfused(**rest, **over) == code
+
+
+def test_unfused_empty_problems_are_no_ops(lib):
+    null = dict(q=None, k=None, v=None, out=None, lse=None)
+    assert call_unfused(B=0, scores=None, scores_bytes=0, **null) == E.ATTN_OK
+    assert call_unfused(s_q=0, scores=None, scores_bytes=0, **null) == E.ATTN_OK
 
 
 # ---------------------------------------------------------------- backward entry point
