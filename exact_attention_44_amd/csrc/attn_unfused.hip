@@ -32,15 +32,18 @@ constexpr int kRows = 128;   // query rows per workgroup (4 waves of 32)
 constexpr int kKeysWG = 1024;  // keys per workgroup of the score kernel
 
 // ---------------------------------------------------------------- 1. scores
-// Workgroup: 128 query rows x up to 1024 keys of one (b, h), in tiles of 128
+// Workgroup: 128 query rows x up to 1024 keys of one (b, h), in tiles of 64
 // keys. Each wave keeps its 32 queries' Q fragments in registers and computes
 // S^T = K Q^T per 32-key block with v_mfma_f32_32x32x16_bf16, K rows fed in
 // the key_of_row order so that accumulator registers 0..7 / 8..15 of lane half
-// h hold keys 8h..8h+7 / 16+8h..16+8h+7 of its query: each lane stores two
-// runs of 8 consecutive scores (16 bytes each) per block. The K tile passes
-// through registers into LDS rows padded by 16 bytes (conflict-free fragment
-// reads), double-buffered, the next tile's loads in flight during the
-// products. VEC (s_k a multiple of 8): 16-byte stores; otherwise 2-byte.
+// h hold keys 8h..8h+7 / 16+8h..16+8h+7 of its query. The wave's 32 x 64
+// block of bf16 scores goes through its own LDS staging area (rows padded by
+// 16 bytes) so that the stores to device memory are whole 128-byte row
+// segments, 8 rows per instruction, instead of 16-byte pieces of 32 rows. The
+// K tile passes through registers into LDS rows padded by 16 bytes
+// (conflict-free fragment reads), double-buffered, the next tile's loads in
+// flight during the products. VEC (s_k a multiple of 8): 16-byte accesses;
+// otherwise 2-byte stores.
 template <int D, bool VEC>
 __global__ __launch_bounds__(256, 2) void unf_scores_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
@@ -48,11 +51,12 @@ __global__ __launch_bounds__(256, 2) void unf_scores_kernel(const uint16_t* __re
                                                            int s_k, int n_qt, int n_kc,
                                                            float scale) {
   constexpr int DK = D / 16;
-  constexpr int KT = 128;             // keys per tile
-  constexpr int KS = D * 2 + 16;      // LDS row stride (bytes)
-  constexpr int UNITS = KT * D / 8;   // 16-byte units per tile
+  constexpr int KT = 64;              // keys per tile
+  constexpr int KS = D * 2 + 16;      // K row stride in LDS (bytes)
+  constexpr int UNITS = KT * D / 8;   // 16-byte units per K tile
   constexpr int UPT = UNITS / 256;    // per thread
-  __shared__ __attribute__((aligned(16))) char lds[2 * KT * KS];
+  constexpr int SS = KT * 2 + 16;     // staging row stride (bytes)
+  __shared__ __attribute__((aligned(16))) char lds[2 * KT * KS + 4 * 32 * SS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, ln = lane & 31;
@@ -89,9 +93,10 @@ __global__ __launch_bounds__(256, 2) void unf_scores_kernel(const uint16_t* __re
     }
   };
 
-  const int row = q0 + 32 * w + ln;
-  uint16_t* srow = S + ((int64_t)bh * s_q + row) * s_k;
+  char* stage = lds + 2 * KT * KS + w * 32 * SS;
   const int k_lane_off = key_of_row(ln) * KS + hl * 16;
+  // store phase: lane l writes 16 bytes of row 8 i + l / 8 at column 16 (l % 8)
+  const int st_row = lane >> 3, st_col = (lane & 7) * 8;
 
   if (n_t > 0) load_tile(0);
   for (int t = 0; t < n_t; ++t) {
@@ -108,24 +113,35 @@ __global__ __launch_bounds__(256, 2) void unf_scores_kernel(const uint16_t* __re
         acc[kb] = mfma(a, qf[kk], kk ? acc[kb] : f32x16_t{});
       }
     }
-    if (row < s_q) {
-      const int jt = jc0 + t * KT;
+    // scaled scores, bf16, into the wave's staging rows (query ln, 8 keys per
+    // 16-byte piece); the wave reads them back row-wise below, after its own
+    // writes (LDS accesses of one wave complete in order)
 #pragma unroll
-      for (int kb = 0; kb < KT / 32; ++kb) {
+    for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int j = jt + 32 * kb + 16 * half + 8 * hl;
-          u32x4_t wv;
+      for (int half = 0; half < 2; ++half) {
+        u32x4_t wv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            wv[e] = pack_bf16(acc[kb][8 * half + 2 * e] * scale, acc[kb][8 * half + 2 * e + 1] * scale);
-          if (VEC) {
-            if (j < s_k) *(u32x4_t*)(srow + j) = wv;
-          } else {
+        for (int e = 0; e < 4; ++e)
+          wv[e] = pack_bf16(acc[kb][8 * half + 2 * e] * scale, acc[kb][8 * half + 2 * e + 1] * scale);
+        *(u32x4_t*)(stage + ln * SS + (32 * kb + 16 * half + 8 * hl) * 2) = wv;
+      }
+    }
+    const int jt = jc0 + t * KT;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (j + e < s_k) srow[j + e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
-          }
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + st_row;
+      const int row = q0 + 32 * w + r;
+      const u32x4_t wv = *(const u32x4_t*)(stage + r * SS + st_col * 2);
+      const int j = jt + st_col;
+      if (row < s_q) {
+        uint16_t* dst = S + ((int64_t)bh * s_q + row) * s_k + j;
+        if (VEC) {
+          if (j < s_k) *(u32x4_t*)dst = wv;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (j + e < s_k) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
         }
       }
     }
