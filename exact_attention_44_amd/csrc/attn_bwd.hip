@@ -107,6 +107,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 
   __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
   __shared__ int lds_last;
+  // With a padding mask: the key tiles that hold a visible key, in order (see
+  // build_tile_list); a longer key range walks every tile up to the last
+  // unpadded key.
+  __shared__ uint16_t lds_tl[PADMASK ? kTileListMax + 8 : 1];
+  __shared__ __attribute__((aligned(8))) uint8_t lds_bits[PADMASK ? kTileListMax / 8 : 8];
+  __shared__ int lds_cnt[3];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -122,8 +128,26 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 
   int kend = s_k;
   if (CAUSAL) kend = min(kend, q0 + BR);
-  if (PADMASK) kend = min(kend, keys_until_last_unpadded(mg, s_k, &lds_last));
-  const int n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
+  const int n_t = kend > 0 ? (kend + BC - 1) / BC : 0;
+  int n_kv = n_t;
+  // walk position u is key tile toff + u, or entry u of the tile list when
+  // the visible tiles are not contiguous
+  int toff = 0, contig = 1;
+  if (PADMASK && n_t <= kTileListMax) {
+    n_kv = build_tile_list<BC, NT / 64>(mg, kend, n_t, lds_bits, lds_tl, lds_cnt, &toff, &contig);
+  } else if (PADMASK) {
+    kend = min(kend, keys_until_last_unpadded(mg, s_k, &lds_last));
+    n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
+  }
+  const bool use_list = PADMASK && contig == 0;
+  // Key tiles at walk positions t .. t + 3 in lanes 0 .. 3 of one register
+  // (t: the current iteration).
+  auto ring_load = [&](int t0) -> int {
+    const int u = t0 + (lane & 3);
+    return use_list ? (int)lds_tl[min(u, kTileListMax + 7)] : toff + u;
+  };
+  int ringv = PADMASK ? ring_load(0) : 0;
+  auto ring_at = [&](int k) -> int { return __builtin_amdgcn_readlane(ringv, k); };
 
   // query side, one query per lane: Q and dO fragments (B operands), O for D
   const int qlo = q0 + 32 * wv;
@@ -168,8 +192,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
     const int r = sl / SL, ph = sl % SL;
     k_voff[i] = (uint32_t)(r * RB + 16 * (ph ^ q_swz<D>(r)));
   }
-  auto dma_tile = [&](int u, int bi) {
-    const int j0 = u * BC;
+  // key tile ti into LDS buffer bi
+  auto dma_tile = [&](int ti, int bi) {
+    const int j0 = ti * BC;
     char* base = lds + bi * BUF;
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * RB;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (int64_t)j0 * D, rest);
@@ -205,15 +230,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
       }
   }
 
-  if (n_kv > 0) dma_tile(0, 0);
+  if (n_kv > 0) dma_tile(PADMASK ? ring_at(0) : 0, 0);
+  uint32_t mbyte = 1u;  // this lane's padding byte of the current tile
   __syncthreads();
   for (int t = 0; t < n_kv; ++t) {
+    // the next iteration's list entries, read before this iteration's loads
+    const int ring_new = PADMASK ? ring_load(t + 1) : 0;
+    const int j0 = (PADMASK ? ring_at(0) : t) * BC;
+    // the padding byte before the tile loads: the vote below then waits for
+    // the byte alone, not for the loads issued after it
+    if (PADMASK) {
+      mbyte = mg[min(j0 + lane, s_k - 1)];
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // the other buffer was last read in the previous iteration, before its
     // closing barrier; this barrier's wait also covers the new loads
-    if (t + 1 < n_kv) dma_tile(t + 1, (t + 1) & 1);
+    if (t + 1 < n_kv) dma_tile(PADMASK ? ring_at(1) : t + 1, (t + 1) & 1);
     const char* kl = lds + (t & 1) * BUF;
     const char* vl = kl + TILE;
-    const int j0 = t * BC;
     // S^T = K Q^T and dP^T = V dO^T, one 32-key block at a time
     f32x16_t sc[KB], dp[KB];
 #pragma unroll
@@ -232,8 +266,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
     // masks: keys past s_k or padded, and causal (key j hidden from row i when j > i)
     uint64_t hid;
     if (PADMASK) {
-      const int key = j0 + lane;
-      hid = __ballot(!(key < s_k && mg[key] == 0));
+      // the byte was requested before the score products, from a clamped
+      // address (a load under a branch would be waited for at once); keys
+      // past s_k are hidden here. Lanes past BC vote on keys of the next
+      // tile; their bits are unused.
+      hid = __ballot(j0 + lane >= s_k || mbyte != 0u);
     } else {
       const int rem = s_k - j0;
       hid = rem >= BC ? 0ull : ~((1ull << rem) - 1ull);
@@ -281,6 +318,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
           dqt[db] = mfma(__builtin_bit_cast(bf16x8_t, a), pf[kb][ks], dqt[db]);
         }
     __syncthreads();
+    if (PADMASK) ringv = ring_new;
   }
 
   if (row < s_q) {
@@ -346,9 +384,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdP
   const bool keys_masked = PADMASK || __ballot(!kvis) != 0ull;
   const int kmax = k0 + 32 * wv + 31;  // this wave's last key
 
-  // query tiles that can see a key of this tile
+  // query tiles that can see a key of this tile; none when every key of the
+  // block is padded (its gradients are zero)
   const int qt0 = CAUSAL ? min(k0, s_q) / BQ : 0;
-  const int qt1 = (s_q + BQ - 1) / BQ;
+  int qt1 = (s_q + BQ - 1) / BQ;
+  if (PADMASK && !__syncthreads_or(kvis)) qt1 = qt0;
   const uint16_t* qg = p.q + (int64_t)bh * s_q * D;
   const uint16_t* dg = p.dout + (int64_t)bh * s_q * D;
   const float* l2g = p.lse2w + (int64_t)bh * p.s_qp;

@@ -6,6 +6,7 @@
 #define EXACT_ATTENTION_44_AMD_ATTN_COMMON_H
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include <atomic>
@@ -179,6 +180,81 @@ __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70
 
 __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+// Largest number of key tiles whose visibility list build_tile_list keeps.
+constexpr int kTileListMax = 4096;
+
+// The key tiles (BC keys each, BC <= 64) among the first n_t tiles of the key
+// range [0, kend) that hold at least one visible key (mask byte mg[j] == 0).
+// Returns their count, the same in every lane. When they are contiguous
+// (padding only before and after them, the usual case) *first gets the first
+// of them and *contig 1, and nothing else is written; otherwise *first gets 0,
+// *contig 0, and tl[0 .. count) lists them in increasing order, followed by 8
+// zero entries. bits is scratch of at least kTileListMax / 8 bytes, 8-byte
+// aligned; cnt holds 3 ints. Every thread of the workgroup (NW waves) calls
+// it: it holds two workgroup barriers. Each wave votes on 8 tiles per step
+// (its lanes read one key each, all eight loads in flight together), writing
+// one byte of a bitmap; then wave 0 reads the bitmap, lane l the 64 tiles of
+// word l: counts by a scan across lanes, first and last tile by reductions,
+// and only when the tiles are not contiguous the list. Requires
+// 0 <= n_t <= kTileListMax and n_t * BC >= kend.
+template <int BC, int NW>
+__device__ __forceinline__ int build_tile_list(const uint8_t* mg, int kend, int n_t, uint8_t* bits,
+                                               uint16_t* tl, int* cnt, int* first, int* contig) {
+  static_assert(BC <= 64, "one key per lane");
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int n_pad = (n_t + 63) & ~63;  // whole bitmap words; bits past n_t are zero
+  for (int s0 = 0; s0 < n_pad; s0 += 8 * NW) {
+    const int u0 = s0 + 8 * wv;
+    uint32_t mb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mb[i] = mg[min((u0 + i) * BC + lane, kend - 1)];  // kend >= 1 here
+    uint32_t b = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = (u0 + i) * BC + lane;
+      const bool vis = lane < BC && u0 + i < n_t && key < kend && mb[i] == 0u;
+      if (__ballot(vis) != 0ull) b |= 1u << i;
+    }
+    if (lane == 0 && u0 < n_pad) bits[u0 >> 3] = (uint8_t)b;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const int nw = n_pad / 64;
+    const uint64_t word = lane < nw ? *(const uint64_t*)(bits + 8 * lane) : 0ull;
+    const int c = __popcll(word);
+    int incl = c;
+    int lo = word ? 64 * lane + __builtin_ctzll(word) : INT_MAX;
+    int hi = word ? 64 * lane + 63 - __builtin_clzll(word) : -1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+      lo = min(lo, __shfl_xor(lo, off));
+      hi = max(hi, __shfl_xor(hi, off));
+    }
+    const int total = __shfl(incl, 63);
+    const bool contiguous = total == 0 || hi - lo + 1 == total;
+    if (!contiguous) {
+      int pos = incl - c;
+      for (uint64_t wd = word; wd != 0ull; wd &= wd - 1ull) tl[pos++] = (uint16_t)(64 * lane + __builtin_ctzll(wd));
+    }
+    if (lane == 63) {
+      cnt[0] = total;
+      cnt[1] = contiguous ? (total ? lo : 0) : 0;
+      cnt[2] = contiguous ? 1 : 0;
+      if (!contiguous) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tl[total + e] = 0;
+      }
+    }
+  }
+  __syncthreads();
+  *first = __builtin_amdgcn_readfirstlane(cnt[1]);
+  *contig = __builtin_amdgcn_readfirstlane(cnt[2]);
+  return __builtin_amdgcn_readfirstlane(cnt[0]);
 }
 
 }  // namespace attn_detail

@@ -118,6 +118,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
 
   __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF_BYTES];
   __shared__ int lds_last;
+  // With a padding mask: the key tiles of the current item that hold at least
+  // one visible key, in order (followed by 8 zero entries), their count, and
+  // a bitmap of tile visibility the list is built from. Items with more than
+  // LIST_MAX tiles walk every tile up to the last unpadded key instead.
+  constexpr int LIST_MAX = kTileListMax;
+  __shared__ uint16_t lds_tl[PADMASK ? LIST_MAX + 8 : 1];
+  __shared__ __attribute__((aligned(8))) uint8_t lds_bits[PADMASK ? LIST_MAX / 8 : 8];
+  __shared__ int lds_cnt[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -205,17 +213,18 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   }
   // K rows of tile u into LDS; completes asynchronously (the next fenced
   // barrier of this wave waits for it).
-  // Tile u of cur (nothing past its last tile).
-  auto src_tile = [&](const uint16_t* base_cur, int u, const uint16_t*& src, uint32_t& bytes) -> bool {
+  // The tile at walk position u of cur is key tile ti (keys ti * BC ..; ti
+  // == u except where a padding mask skips tiles); nothing past the walk.
+  auto src_tile = [&](const uint16_t* base_cur, int u, int ti, const uint16_t*& src, uint32_t& bytes) -> bool {
     if (u >= n_kv) return false;
-    src = base_cur + (int64_t)u * BC * D;
-    bytes = (uint32_t)max(s_kc - u * BC, 0) * D * 2;
+    src = base_cur + (int64_t)ti * BC * D;
+    bytes = (uint32_t)max(s_kc - ti * BC, 0) * D * 2;
     return true;
   };
-  auto dma_k = [&](int u) {
+  auto dma_k = [&](int u, int ti) {
     const uint16_t* src;
     uint32_t rest;
-    if (!src_tile(kg, u, src, rest)) return;
+    if (!src_tile(kg, u, ti, src, rest)) return;
     const __amdgpu_buffer_rsrc_t rkt = make_rsrc(src, rest);
     char* kl = lds + ((boff + u) & (NBUF - 1)) * BUF_BYTES + grp * K_SLOTS * 16;
 #pragma unroll
@@ -237,10 +246,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     v_voff[i] = (uint32_t)(r * D + (un < KU ? 8 * un : 0)) * 2;
   }
   // V rows of tile u into LDS, the same way as K (VDMA).
-  auto dma_v = [&](int u) {
+  auto dma_v = [&](int u, int ti) {
     const uint16_t* src;
     uint32_t rest;
-    if (!src_tile(vg, u, src, rest)) return;
+    if (!src_tile(vg, u, ti, src, rest)) return;
     const __amdgpu_buffer_rsrc_t rvt = make_rsrc(src, rest);
     char* vl = lds + ((boff + u) & (NBUF - 1)) * BUF_BYTES + K_BYTES + grp * V_SLOTS * 16;
 #pragma unroll
@@ -252,8 +261,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // V through registers (not VDMA): load_v(u) fetches this thread's item of
   // tile u of cur (zeros past its end), store_v(u) writes it transposed.
   u32x4_t vr[V_LD][2];
-  auto load_v = [&](int u) {
-    const int j0 = u * BC;
+  auto load_v = [&](int ti) {
+    const int j0 = ti * BC;
     const uint32_t rest = (uint32_t)max(s_kc - j0, 0) * D * 2;
     const __amdgpu_buffer_rsrc_t rvt = make_rsrc(vg + (int64_t)j0 * D, rest);
 #pragma unroll
@@ -290,6 +299,23 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   f32x16_t sc[KB];         // scores of the tile between its two steps
   bf16x8_t pf[KB][2];      // weights of the tile between its two steps
   uint32_t mbyte = 1u;     // this lane's padding byte of the tile in flight
+  // Walk position u of the current item is key tile toff + u, unless the
+  // item's visible tiles are not contiguous: then it walks its tile list
+  // (lds_tl), the tile walk below is instantiated for that case separately
+  // (list = std::true_type), and each wave keeps the tiles at positions
+  // t .. t + 3 in lanes 0 .. 3 of one register (t: the tile the next V step
+  // handles). One vector register rather than four scalar ones: the kernel's
+  // scalar registers are nearly all in use. The contiguous case keeps the
+  // loop free of the list's reads.
+  int toff = 0;
+  bool use_list = false;
+  int ringv = 0;
+  auto ring_load = [&](int t0) -> int { return (int)lds_tl[min(t0 + (lane & 3), kTileListMax + 7)]; };
+  // key tile at walk position t + k (k = 0 .. 3) while position t is the next V step's
+  auto tile_at = [&](int t, int k, auto list) __attribute__((always_inline)) -> int {
+    if constexpr (decltype(list)::value) return __builtin_amdgcn_readlane(ringv, k);
+    else return toff + t + k;
+  };
 
   const int k_lane_off = key_of_row(ln) * KS + hl * 16;
   // VDMA: transpose-read offset of V^T: read r (0, 1) of feature block db
@@ -337,7 +363,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // M step, second half: S(t)^T = K_t Q^T. The key blocks' accumulation
   // chains are interleaved (k-step outer), so consecutive MFMAs never depend
   // on each other's result.
-  auto qk = [&](int t) {
+  auto qk = [&](int t, auto list) __attribute__((always_inline)) {
     const char* kl = lds + ((boff + t) & (NBUF - 1)) * BUF_BYTES + k_lane_off;
     f32x16_t acc[KB];
 #pragma unroll
@@ -351,7 +377,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sc[kb] = acc[kb];
     if (PADMASK) {
-      const int key = t * BC + lane;
+      const int key = tile_at(t, 0, list) * BC + lane;
       mbyte = key < s_kc ? (uint32_t)mg[key] : 1u;
     }
   };
@@ -363,13 +389,13 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int N_PV = KB * 2 * DB;            // value-product MFMAs per M step
   constexpr int N_MF = N_PV + KB * DK;         // MFMAs (= fragments) per M step
   static_assert(LA <= N_PV, "prefetched fragments must belong to the value product");
-  auto m_step = [&](int tp, int tq) {
+  auto m_step = [&](int tp, int tq, auto list) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(2);
     pv(tp);
-    qk(tq);
+    qk(tq, list);
     if constexpr (!VDMA) {
       store_v(tq + 1);
-      load_v(tq + 2);
+      load_v(tile_at(tq, 2, list));
     }
 #pragma unroll
     for (int i = 0; i < N_PV - LA; ++i) {
@@ -386,10 +412,15 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     __builtin_amdgcn_s_setprio(0);
   };
   // V step: masks and online softmax of S(t) -> P(t).
-  auto vstep = [&](int t) {
-    dma_k(t + 3);
-    if constexpr (VDMA) dma_v(t + 2);
-    const int j0 = t * BC;
+  auto vstep = [&](int t, auto list) __attribute__((always_inline)) {
+    constexpr bool LIST = decltype(list)::value;
+    // the next four list entries, requested before this step's loads into
+    // LDS so the compiler has no reason to wait for those loads here
+    int ring_new = 0;
+    if constexpr (LIST) ring_new = ring_load(t + 1);
+    dma_k(t + 3, tile_at(t, 3, list));
+    if constexpr (VDMA) dma_v(t + 2, tile_at(t, 2, list));
+    const int j0 = tile_at(t, 0, list) * BC;
     // hidden-key bits of the tile (padding, keys past s_k); wave-uniform
     uint64_t hid;
     if (PADMASK) {
@@ -488,6 +519,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       rs = weights();
     }
     l_run += rs;
+    if constexpr (LIST) ringv = ring_new;
   };
 
   // ---- the workgroup's items, one after the other
@@ -501,11 +533,20 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     vg = p.v + ((int64_t)cur.bh * s_k + k0) * D;
     mg = PADMASK ? p.kpm + (int64_t)cur.b * s_k + k0 : nullptr;
     qlo = cur.q0 + 32 * wv;
-    // keys this tile can see: causal stops at the last query row; padding
-    // stops after the last key that is not padded.
+    // keys this tile can see: causal stops at the last query row; with a
+    // padding mask only the tiles that hold a visible key are walked.
     int kend = s_kc;
     if (CAUSAL) kend = min(kend, cur.q0 + BR - k0);
-    if (PADMASK) {
+    const int n_t = kend > 0 ? (kend + BC - 1) / BC : 0;
+    toff = 0;
+    use_list = false;
+    if (PADMASK && n_t <= LIST_MAX) {
+      int contig = 1;
+      n_kv = build_tile_list<BC, NT / 64>(mg, kend, n_t, lds_bits, lds_tl, lds_cnt, &toff, &contig);
+      // contiguous visible tiles are walked as a range, others through the list
+      use_list = contig == 0;
+    } else if (PADMASK) {
+      // a long item: walk every tile up to the last key that is not padded
       if (tid == 0) lds_last = -1;
       __syncthreads();
       int last = -1;
@@ -529,22 +570,30 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
         }
       }
       kend = min(kend, last + 1);
+      n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
+    } else {
+      n_kv = n_t;
     }
-    n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
     load_q(cur);
+    // the first tiles' loads (positions 0 .. 2); selects rather than a branch
+    // on the kind of walk
+    if (PADMASK) ringv = ring_load(0);
+    auto first_tile = [&](int k) -> int {
+      return (PADMASK && use_list) ? __builtin_amdgcn_readlane(ringv, k) : toff + k;
+    };
     if (n_kv > 0) {
-      dma_k(0);
-      dma_k(1);
-      dma_k(2);
+      dma_k(0, first_tile(0));
+      dma_k(1, first_tile(1));
+      dma_k(2, first_tile(2));
       if constexpr (VDMA) {
-        dma_v(0);
-        dma_v(1);
+        dma_v(0, first_tile(0));
+        dma_v(1, first_tile(1));
       } else {
-        load_v(0);
+        load_v(first_tile(0));
         store_v(0);
-        load_v(1);
+        load_v(first_tile(1));
         store_v(1);
-        load_v(2);
+        load_v(first_tile(2));
       }
     }
     __syncthreads();
@@ -590,36 +639,42 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       for (int i = 0; i < LA; ++i) vpre[i] = v_frag(t, i);
       __builtin_amdgcn_sched_barrier(0);
     };
-    if (n_kv > 0) {
+    auto walk = [&](auto list) __attribute__((always_inline)) {
       if (grp == 0) {
-        qk(0);
+        qk(0, list);
         phase_sync();
         for (int t = 0; t < n_kv - 1; ++t) {
-          vstep(t);
+          vstep(t, list);
           vstep_end(t);
-          m_step(t, t + 1);
-            phase_sync();
+          m_step(t, t + 1, list);
+          phase_sync();
         }
-        vstep(n_kv - 1);
+        vstep(n_kv - 1, list);
         vstep_end(n_kv - 1);
         pv(n_kv - 1);
         phase_sync();
         phase_sync();
       } else {
         phase_sync();
-        qk(0);
-        vstep(0);
+        qk(0, list);
+        vstep(0, list);
         vstep_end(0);
         phase_sync();
         for (int t = 1; t < n_kv; ++t) {
-          m_step(t - 1, t);
-          vstep(t);
+          m_step(t - 1, t, list);
+          vstep(t, list);
           vstep_end(t);
           phase_sync();
         }
         pv(n_kv - 1);
         phase_sync();
       }
+    };
+    if (n_kv > 0) {
+      if (PADMASK && use_list)
+        walk(std::true_type{});
+      else
+        walk(std::false_type{});
     }
 
     // ---- epilogue: O = O^T / l, lse = m * |scale| + ln(l)

@@ -40,6 +40,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn.h"
 #include "attn_common.h"
 
@@ -114,6 +116,12 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
 
   __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF_BYTES];
   __shared__ int lds_last;
+  // With a padding mask: the key tiles of the current item that hold a
+  // visible key, in order (see build_tile_list); items with more tiles than
+  // the list holds walk every tile up to the last unpadded key.
+  __shared__ uint16_t lds_tl[PADMASK ? kTileListMax + 8 : 1];
+  __shared__ __attribute__((aligned(8))) uint8_t lds_bits[PADMASK ? kTileListMax / 8 : 8];
+  __shared__ int lds_cnt[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -158,15 +166,16 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   // The tile loads are untracked by the compiler (which would otherwise wait
   // for them before the next LDS read of any buffer); every fenced barrier
   // below waits for them explicitly.
-  auto dma_k = [&](int u) {
-    const int j0 = u * BC;
+  // position u of the walk (LDS buffer) is key tile ti (keys ti * BC ..)
+  auto dma_k = [&](int u, int ti) __attribute__((always_inline)) {
+    const int j0 = ti * BC;
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D;
     if (wg < N_DMA)
       load16_to_lds_untracked(kg + (int64_t)j0 * D, rest,
                               lds + ((boff + u) & (NBUF - 1)) * BUF_BYTES + (grp * H_SLOTS + 64 * wg) * 16, k_voff);
   };
-  auto dma_v = [&](int u) {
-    const int j0 = u * BC;
+  auto dma_v = [&](int u, int ti) __attribute__((always_inline)) {
+    const int j0 = ti * BC;
     const uint32_t rest = (uint32_t)max(s_k - j0, 0) * D;
     if (wg < N_DMA)
       load16_to_lds_untracked(vg + (int64_t)j0 * D, rest,
@@ -180,6 +189,22 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   float xw[KB][16];        // float32 weights of the tile between its two steps
   i32x8_t pf;              // the same rounded to E4M3 (value product operand)
   uint32_t mbyte = 1u;
+  // Walk position u of the current item is key tile toff + u, unless the
+  // item's visible tiles are not contiguous: then it walks its tile list
+  // (lds_tl), the tile walk is instantiated for that case separately (list =
+  // std::true_type), and each wave keeps the tiles at positions t .. t + 3 in
+  // lanes 0 .. 3 of one register (t: the tile the next V step handles; one
+  // vector register, as the scalar ones are nearly all in use). The
+  // contiguous case keeps the loop free of the list's reads.
+  int toff = 0;
+  bool use_list = false;
+  int ringv = 0;
+  auto ring_load = [&](int t0) -> int { return (int)lds_tl[min(t0 + (lane & 3), kTileListMax + 7)]; };
+  // key tile at walk position t + k (k = 0 .. 3) while position t is the next V step's
+  auto tile_at = [&](int t, int k, auto list) __attribute__((always_inline)) -> int {
+    if constexpr (decltype(list)::value) return __builtin_amdgcn_readlane(ringv, k);
+    else return toff + t + k;
+  };
 
   // Score-product fragment reads: lane (ln, hl) reads K row 32 kb + ln at
   // logical slot 4 kk + 2 hl + u (features 64 kk + 32 hl + 16 u ..); the
@@ -204,7 +229,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     for (int db = 0; db < DB; ++db)
       v_off[db] = row * D + 16 * (2 * (db ^ sw) + ((lane >> 4) & 1)) + 8 * (lane & 1);
   }
-  auto v_read = [&](int t, int i) -> i32x2_t {
+  auto v_read = [&](int t, int i) __attribute__((always_inline)) -> i32x2_t {
     // read i of tile t's value product: feature block i / 4, byte block i % 4
     const char* vl = lds + ((boff + t) & (NBUF - 1)) * BUF_BYTES + K_BYTES;
     const int db = i >> 2, tb = i & 3;
@@ -220,11 +245,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   // product's K fragments.
   i32x2_t vr[N_VR];
   i32x8_t ka[KB][DK];
-  auto read_v = [&](int t) {
+  auto read_v = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < N_VR; ++i) vr[i] = i < LA ? vpre[i < LA ? i : 0] : v_read(t, i);
   };
-  auto read_k = [&](int t) {
+  auto read_k = [&](int t) __attribute__((always_inline)) {
     const char* kl = lds + ((boff + t) & (NBUF - 1)) * BUF_BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -238,7 +263,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
         }
   };
   // O^T += V_t^T P(t)^T.
-  auto pv_mfma = [&]() {
+  auto pv_mfma = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       i32x8_t a;
@@ -251,7 +276,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     }
   };
   // S(t)^T = K_t Q^T (the key blocks' chains interleaved).
-  auto qk_mfma = [&](int t) {
+  auto qk_mfma = [&](int t, auto list) __attribute__((always_inline)) {
     f32x16_t acc[KB];
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk)
@@ -260,13 +285,13 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sc[kb] = acc[kb];
     if (PADMASK) {
-      const int key = t * BC + lane;
+      const int key = tile_at(t, 0, list) * BC + lane;
       mbyte = key < s_k ? (uint32_t)mg[key] : 1u;
     }
   };
-  auto qk = [&](int t) {
+  auto qk = [&](int t, auto list) __attribute__((always_inline)) {
     read_k(t);
-    qk_mfma(t);
+    qk_mfma(t, list);
   };
   // Weights of the scores in sc against the current reference max.
   auto weights = [&](float nmc) __attribute__((always_inline)) {
@@ -328,21 +353,25 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   };
   // One M step: every LDS read first, then the softmax tail (its vector work
   // covers the read latency), then the eight MFMAs.
-  auto m_step = [&](int tp, int tq) {
+  auto m_step = [&](int tp, int tq, auto list) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(2);
     read_v(tp);
     read_k(tq);
     finish();
     pv_mfma();
-    qk_mfma(tq);
+    qk_mfma(tq, list);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
   };
   // V step: staging of later tiles, then masks and the exponentials of S(t).
-  auto vstep = [&](int t) {
-    dma_k(t + 3);
-    dma_v(t + 2);
-    const int j0 = t * BC;
+  auto vstep = [&](int t, auto list) __attribute__((always_inline)) {
+    constexpr bool LIST = decltype(list)::value;
+    // the next four list entries, read before this step's loads
+    int ring_new = 0;
+    if constexpr (LIST) ring_new = ring_load(t + 1);
+    dma_k(t + 3, tile_at(t, 3, list));
+    dma_v(t + 2, tile_at(t, 2, list));
+    const int j0 = tile_at(t, 0, list) * BC;
     uint64_t hid;
     if (PADMASK) {
       hid = __ballot(mbyte != 0u);
@@ -375,6 +404,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
       if (m_run == -INFINITY) m_run = mx;
     }
     weights(-((m_run == -INFINITY) ? 0.f : m_run) * c);
+    if constexpr (LIST) ringv = ring_new;
   };
 
   // ---- the workgroup's items, one after the other
@@ -404,11 +434,20 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     vg = p.v + (int64_t)bh * s_k * D;
     mg = PADMASK ? p.kpm + (int64_t)b * s_k : nullptr;
 
-    // ---- keys this tile can see (causal: up to the last query row; padding:
-    // up to the last key that is not padded)
+    // ---- keys this tile can see: causal stops at the last query row; with a
+    // padding mask only the tiles that hold a visible key are walked
     int kend = s_k;
     if (CAUSAL) kend = min(kend, q0 + BR);
-    if (PADMASK) {
+    const int n_t = kend > 0 ? (kend + BC - 1) / BC : 0;
+    toff = 0;
+    use_list = false;
+    if (PADMASK && n_t <= kTileListMax) {
+      int contig = 1;
+      n_kv = build_tile_list<BC, NT / 64>(mg, kend, n_t, lds_bits, lds_tl, lds_cnt, &toff, &contig);
+      // contiguous visible tiles are walked as a range, others through the list
+      use_list = contig == 0;
+    } else if (PADMASK) {
+      // a long item: walk every tile up to the last key that is not padded
       if (tid == 0) lds_last = -1;
       __syncthreads();
       int last = -1;
@@ -432,8 +471,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
         }
       }
       kend = min(kend, last + 1);
+      n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
+    } else {
+      n_kv = n_t;
     }
-    n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
 
     // ---- Q (B operand of the score product): lane holds query qlo + ln,
     // features 64 kk + 32 hl .. +31
@@ -457,12 +498,18 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     l_run = 0.f;
     mbyte = 1u;
 
+    // the first tiles' loads (positions 0 .. 2); selects rather than a branch
+    // on the kind of walk (a branch here made the compiler spill)
+    if (PADMASK) ringv = ring_load(0);
+    auto first_tile = [&](int k) -> int {
+      return (PADMASK && use_list) ? __builtin_amdgcn_readlane(ringv, k) : toff + k;
+    };
     if (n_kv > 0) {
-      dma_k(0);
-      dma_k(1);
-      dma_k(2);
-      dma_v(0);
-      dma_v(1);
+      dma_k(0, first_tile(0));
+      dma_k(1, first_tile(1));
+      dma_k(2, first_tile(2));
+      dma_v(0, first_tile(0));
+      dma_v(1, first_tile(1));
     }
     wait_loads();
     __syncthreads();
@@ -478,7 +525,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     // (interval u + 2). Every request comes after the last read of tile u - 4
     // (K: interval u - 3, V: interval u - 2) and is waited for (explicitly: the
     // requests are untracked) at the barrier closing its interval.
-    auto phase_sync = [&]() {
+    auto phase_sync = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
       wait_loads();
       __syncthreads();
@@ -486,23 +533,23 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     };
     // End of V(t): the first LA reads of PV(t) are issued here, so their
     // latency overlaps the switch to the M step.
-    auto vstep_end = [&](int t) {
+    auto vstep_end = [&](int t) __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < LA; ++i) vpre[i] = v_read(t, i);
       __builtin_amdgcn_sched_barrier(0);
     };
-    if (n_kv > 0) {
+    auto walk = [&](auto list) __attribute__((always_inline)) {
       if (grp == 0) {
-        qk(0);
+        qk(0, list);
         phase_sync();
         for (int t = 0; t < n_kv - 1; ++t) {
-          vstep(t);
+          vstep(t, list);
           vstep_end(t);
-          m_step(t, t + 1);
+          m_step(t, t + 1, list);
           phase_sync();
         }
-        vstep(n_kv - 1);
+        vstep(n_kv - 1, list);
         vstep_end(n_kv - 1);
         read_v(n_kv - 1);
         finish();
@@ -511,13 +558,13 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
         phase_sync();
       } else {
         phase_sync();
-        qk(0);
-        vstep(0);
+        qk(0, list);
+        vstep(0, list);
         vstep_end(0);
         phase_sync();
         for (int t = 1; t < n_kv; ++t) {
-          m_step(t - 1, t);
-          vstep(t);
+          m_step(t - 1, t, list);
+          vstep(t, list);
           vstep_end(t);
           phase_sync();
         }
@@ -526,6 +573,12 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
         pv_mfma();
         phase_sync();
       }
+    };
+    if (n_kv > 0) {
+      if (PADMASK && use_list)
+        walk(std::true_type{});
+      else
+        walk(std::false_type{});
     }
 
     // ---- epilogue: O = dv * O^T / l, lse = m |scale dq dk| + ln(l)

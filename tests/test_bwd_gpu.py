@@ -75,6 +75,16 @@ CASES = {
     "all_padded": (59, 2, 1, 64, 100, 64, dict(mask="all")),
     "one_key": (60, 1, 2, 70, 1, 128, {}),
     "many_key_tiles": (61, 1, 1, 96, 1100, 128, {}),
+    # whole tiles and 128-key blocks of padding inside the sequence: the dq
+    # kernel does not walk those tiles, the dk/dv kernel skips those blocks
+    "interior_padding_causal_d128": (62, 2, 2, 300, 2000, 128, dict(mask="blocks", causal=True)),
+    "interior_padding_d64": (63, 2, 2, 260, 1800, 64, dict(mask="blocks")),
+    # left padding: the visible tiles are one range that starts past key 0
+    "prefix_padding_causal_d128": (65, 2, 2, 300, 1000, 128, dict(mask="prefix", causal=True)),
+    "prefix_padding_d64": (66, 2, 2, 260, 900, 64, dict(mask="prefix")),
+    # more 32-key tiles than the tile list holds: the dq kernel walks every
+    # tile up to the last unpadded key
+    "interior_padding_beyond_list_d128": (64, 1, 1, 24, 4096 * 32 + 700, 128, dict(mask="blocks")),
 }
 
 

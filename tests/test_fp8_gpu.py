@@ -157,6 +157,13 @@ EDGE_CASES = {
     # own descales, a partial last round
     "rounds_causal_d64": (119, 3, 37, 600, 600, 64, dict(causal=True)),
     "rounds_lengths_d64": (120, 6, 16, 700, 650, 64, dict(mask="lengths")),
+    # whole 64-key tiles of padding inside the sequence: those tiles are not walked
+    "interior_padding_causal_d128": (121, 2, 2, 700, 3000, 128, dict(mask="blocks", causal=True)),
+    "interior_padding_rounds_d64": (122, 4, 24, 520, 2100, 64, dict(mask="blocks")),
+    # left padding: the visible tiles are one range that starts past key 0
+    "prefix_padding_causal_d128": (124, 2, 2, 900, 2000, 128, dict(mask="prefix", causal=True)),
+    "prefix_padding_rounds_d64": (125, 4, 24, 520, 1500, 64, dict(mask="prefix")),
+    "interior_padding_beyond_list": (123, 1, 1, 20, 4096 * 64 + 900, 64, dict(mask="blocks")),
 }
 
 

@@ -43,6 +43,17 @@ EDGE_CASES = {
     # more items than CUs, a partial last round, heads not a multiple of 8
     "rounds_causal_d64": (18, 3, 37, 600, 600, 64, dict(causal=True)),
     "rounds_lengths_d64": (19, 6, 16, 700, 650, 64, dict(mask="lengths")),
+    # whole 64-key tiles of padding inside the sequence (tiles 8 .. 23 and a
+    # ragged block near the end): those tiles are not walked
+    "interior_padding_causal_d128": (22, 2, 2, 700, 3000, 128, dict(mask="blocks", causal=True)),
+    "interior_padding_d64": (23, 3, 3, 300, 2600, 64, dict(mask="blocks")),
+    "interior_padding_rounds_d64": (24, 4, 24, 520, 2100, 64, dict(mask="blocks", causal=True)),
+    # more key tiles than the tile list holds (4096): the walk covers every
+    # tile up to the last unpadded key instead
+    # left padding: the visible tiles are one range that starts past key 0
+    "prefix_padding_causal_d128": (26, 2, 2, 900, 2000, 128, dict(mask="prefix", causal=True)),
+    "prefix_padding_rounds_d64": (27, 4, 24, 520, 1500, 64, dict(mask="prefix")),
+    "interior_padding_beyond_list": (25, 2, 1, 40, 4096 * 64 + 900, 64, dict(mask="blocks")),
 }
 
 

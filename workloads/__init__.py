@@ -200,7 +200,12 @@ def random_case(seed: int, B: int, H: int, s_q: int, s_k: int, d: int, *,
 
     mask: "none"; "lengths" (valid length per sequence ~ U{0..s_k}); "random"
     (each key padded independently with probability 1/2, so the mask is not a
-    suffix); "all" (every key padded).
+    suffix); "all" (every key padded); "blocks" (interior blocks padded: keys
+    512 .. 1535, so 64-key tiles 8 .. 23 hold no visible key, and a ragged
+    block from s_k - 700 to s_k - 300, in every sequence; sequence 0 also
+    pads its first 200 keys and sequence 1, if any, its last 100); "prefix"
+    (the first s_k / 3 keys of every sequence padded, as in left-padded
+    batches; sequence 1, if any, also pads its last 50).
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     q = _draw(rng, (B, H, s_q, d), q_mult)
@@ -214,6 +219,18 @@ def random_case(seed: int, B: int, H: int, s_q: int, s_k: int, d: int, *,
         kpm = (rng.random((B, s_k)) < 0.5).astype(np.uint8)
     elif mask == "all":
         kpm = np.ones((B, s_k), dtype=np.uint8)
+    elif mask == "blocks":
+        kpm = np.zeros((B, s_k), dtype=np.uint8)
+        kpm[:, 512:1536] = 1
+        kpm[:, max(0, s_k - 700):max(0, s_k - 300)] = 1
+        kpm[0, :200] = 1
+        if B > 1:
+            kpm[1, max(0, s_k - 100):] = 1
+    elif mask == "prefix":
+        kpm = np.zeros((B, s_k), dtype=np.uint8)
+        kpm[:, :s_k // 3] = 1
+        if B > 1:
+            kpm[1, max(0, s_k - 50):] = 1
     elif mask != "none":
         raise ValueError(f"unknown mask kind {mask!r}")
     sc = scale_for(d) if scale is None else np.float32(scale)
