@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   // unpadded key.
   __shared__ uint16_t lds_tl[PADMASK ? kTileListMax + 8 : 1];
   __shared__ __attribute__((aligned(8))) uint8_t lds_bits[PADMASK ? kTileListMax / 8 : 8];
-  __shared__ int lds_cnt[3];
+  __shared__ int lds_scr[3 * (NT / 64) + 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -134,7 +134,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   // the visible tiles are not contiguous
   int toff = 0, contig = 1;
   if (PADMASK && n_t <= kTileListMax) {
-    n_kv = build_tile_list<BC, NT / 64>(mg, kend, n_t, lds_bits, lds_tl, lds_cnt, &toff, &contig);
+    int ka = 0, kb = 0;
+    n_kv = build_tile_list<BC, NT / 64>(mg, kend, n_t, lds_bits, lds_tl, lds_scr, &ka, &kb, &contig);
+    if (contig) {  // visible keys [ka, kb): their tiles as a range
+      toff = ka / BC;
+      n_kv = kb > ka ? (kb - 1) / BC - toff + 1 : 0;
+    }
   } else if (PADMASK) {
     kend = min(kend, keys_until_last_unpadded(mg, s_k, &lds_last));
     n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;

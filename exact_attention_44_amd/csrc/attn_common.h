@@ -185,27 +185,30 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t byt
 // Largest number of key tiles whose visibility list build_tile_list keeps.
 constexpr int kTileListMax = 4096;
 
-// The key tiles (BC keys each, BC <= 64) among the first n_t tiles of the key
-// range [0, kend) that hold at least one visible key (mask byte mg[j] == 0).
-// Returns their count, the same in every lane. When they are contiguous
-// (padding only before and after them, the usual case) *first gets the first
-// of them and *contig 1, and nothing else is written; otherwise *first gets 0,
-// *contig 0, and tl[0 .. count) lists them in increasing order, followed by 8
-// zero entries. bits is scratch of at least kTileListMax / 8 bytes, 8-byte
-// aligned; cnt holds 3 ints. Every thread of the workgroup (NW waves) calls
-// it: it holds two workgroup barriers. Each wave votes on 8 tiles per step
-// (its lanes read one key each, all eight loads in flight together), writing
-// one byte of a bitmap; then wave 0 reads the bitmap, lane l the 64 tiles of
-// word l: counts by a scan across lanes, first and last tile by reductions,
-// and only when the tiles are not contiguous the list. Requires
-// 0 <= n_t <= kTileListMax and n_t * BC >= kend.
+// Visibility of the keys [0, kend) of a work item, from its padding mask
+// (mg[j] == 0: key j visible), in BC-key tiles (BC <= 64), n_t of them.
+// Returns the number of tiles that hold a visible key, the same in every
+// lane, and sets *ka, *kb to the first visible key and one past the last
+// (0, 0 when none). When the visible keys are exactly [ka, kb) (padding only
+// before and after them, the usual case) *contig is 1 and nothing else is
+// written; otherwise *contig is 0 and tl[0 .. count) lists the tiles that
+// hold a visible key, in increasing order, followed by 8 zero entries.
+// bits: scratch of at least kTileListMax / 8 bytes, 8-byte aligned; scr:
+// 3 * NW + 4 ints. Every thread of the workgroup (NW waves) calls it: it
+// holds two workgroup barriers. Each wave votes on 8 tiles per step (its lanes
+// read one key each, all eight loads in flight together), writing one byte of
+// a bitmap and keeping its count of visible keys and their first and last;
+// then wave 0 combines the waves' counts and, only when the visible keys are
+// not one interval, lists the tiles from the bitmap (lane l: the 64 tiles of
+// word l). Requires 0 <= n_t <= kTileListMax and n_t * BC >= kend.
 template <int BC, int NW>
 __device__ __forceinline__ int build_tile_list(const uint8_t* mg, int kend, int n_t, uint8_t* bits,
-                                               uint16_t* tl, int* cnt, int* first, int* contig) {
+                                               uint16_t* tl, int* scr, int* ka, int* kb, int* contig) {
   static_assert(BC <= 64, "one key per lane");
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int n_pad = (n_t + 63) & ~63;  // whole bitmap words; bits past n_t are zero
+  int nk = 0, lo = INT_MAX, hi = -1;   // this wave's visible keys (wave-uniform)
   for (int s0 = 0; s0 < n_pad; s0 += 8 * NW) {
     const int u0 = s0 + 8 * wv;
     uint32_t mb[8];
@@ -216,45 +219,74 @@ __device__ __forceinline__ int build_tile_list(const uint8_t* mg, int kend, int 
     for (int i = 0; i < 8; ++i) {
       const int key = (u0 + i) * BC + lane;
       const bool vis = lane < BC && u0 + i < n_t && key < kend && mb[i] == 0u;
-      if (__ballot(vis) != 0ull) b |= 1u << i;
+      const uint64_t v = __ballot(vis);
+      if (v != 0ull) {
+        b |= 1u << i;
+        nk += __popcll(v);
+        lo = min(lo, (u0 + i) * BC + (int)__builtin_ctzll(v));
+        hi = max(hi, (u0 + i) * BC + 63 - (int)__builtin_clzll(v));
+      }
     }
     if (lane == 0 && u0 < n_pad) bits[u0 >> 3] = (uint8_t)b;
   }
+  if (lane == 0) {
+    scr[3 * wv] = nk;
+    scr[3 * wv + 1] = lo;
+    scr[3 * wv + 2] = hi;
+  }
   __syncthreads();
   if (wv == 0) {
+    const int wnk = lane < NW ? scr[3 * lane] : 0;
+    int wlo = lane < NW ? scr[3 * lane + 1] : INT_MAX;
+    int whi = lane < NW ? scr[3 * lane + 2] : -1;
+    int keys = wnk;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      keys += __shfl_xor(keys, off);
+      wlo = min(wlo, __shfl_xor(wlo, off));
+      whi = max(whi, __shfl_xor(whi, off));
+    }
+    const bool one_interval = keys == 0 || whi - wlo + 1 == keys;
     const int nw = n_pad / 64;
     const uint64_t word = lane < nw ? *(const uint64_t*)(bits + 8 * lane) : 0ull;
     const int c = __popcll(word);
     int incl = c;
-    int lo = word ? 64 * lane + __builtin_ctzll(word) : INT_MAX;
-    int hi = word ? 64 * lane + 63 - __builtin_clzll(word) : -1;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(incl, off);
       if (lane >= off) incl += y;
-      lo = min(lo, __shfl_xor(lo, off));
-      hi = max(hi, __shfl_xor(hi, off));
     }
     const int total = __shfl(incl, 63);
-    const bool contiguous = total == 0 || hi - lo + 1 == total;
-    if (!contiguous) {
+    if (!one_interval) {
       int pos = incl - c;
       for (uint64_t wd = word; wd != 0ull; wd &= wd - 1ull) tl[pos++] = (uint16_t)(64 * lane + __builtin_ctzll(wd));
     }
     if (lane == 63) {
-      cnt[0] = total;
-      cnt[1] = contiguous ? (total ? lo : 0) : 0;
-      cnt[2] = contiguous ? 1 : 0;
-      if (!contiguous) {
+      scr[3 * NW] = total;
+      scr[3 * NW + 1] = keys ? wlo : 0;
+      scr[3 * NW + 2] = keys ? whi + 1 : 0;
+      scr[3 * NW + 3] = one_interval ? 1 : 0;
+      if (!one_interval) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) tl[total + e] = 0;
       }
     }
   }
   __syncthreads();
-  *first = __builtin_amdgcn_readfirstlane(cnt[1]);
-  *contig = __builtin_amdgcn_readfirstlane(cnt[2]);
-  return __builtin_amdgcn_readfirstlane(cnt[0]);
+  *ka = __builtin_amdgcn_readfirstlane(scr[3 * NW + 1]);
+  *kb = __builtin_amdgcn_readfirstlane(scr[3 * NW + 2]);
+  *contig = __builtin_amdgcn_readfirstlane(scr[3 * NW + 3]);
+  return __builtin_amdgcn_readfirstlane(scr[3 * NW]);
+}
+
+// Hidden-key bits of the BC-key tile starting at key j0 when the visible keys
+// are exactly [ka, kb): bit l set when key j0 + l is outside that range
+// (bits past BC are set too). Wave-uniform, scalar arithmetic only.
+__device__ __forceinline__ uint64_t hidden_outside(int j0, int ka, int kb) {
+  const int lo = min(max(ka - j0, 0), 64), hi = min(max(kb - j0, 0), 64);
+  const uint64_t below_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+  const uint64_t below_lo = lo >= 64 ? ~0ull : ((1ull << lo) - 1ull);
+  return ~(below_hi & ~below_lo);
 }
 
 }  // namespace attn_detail

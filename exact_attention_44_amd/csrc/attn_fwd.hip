@@ -125,7 +125,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int LIST_MAX = kTileListMax;
   __shared__ uint16_t lds_tl[PADMASK ? LIST_MAX + 8 : 1];
   __shared__ __attribute__((aligned(8))) uint8_t lds_bits[PADMASK ? LIST_MAX / 8 : 8];
-  __shared__ int lds_cnt[3];
+  __shared__ int lds_scr[3 * (NT / 64) + 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -299,18 +299,24 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   f32x16_t sc[KB];         // scores of the tile between its two steps
   bf16x8_t pf[KB][2];      // weights of the tile between its two steps
   uint32_t mbyte = 1u;     // this lane's padding byte of the tile in flight
-  // Walk position u of the current item is key tile toff + u, unless the
-  // item's visible tiles are not contiguous: then it walks its tile list
-  // (lds_tl), the tile walk below is instantiated for that case separately
-  // (list = std::true_type), and each wave keeps the tiles at positions
-  // t .. t + 3 in lanes 0 .. 3 of one register (t: the tile the next V step
-  // handles). One vector register rather than four scalar ones: the kernel's
-  // scalar registers are nearly all in use. The contiguous case keeps the
-  // loop free of the list's reads.
-  int toff = 0;
-  bool use_list = false;
+  // Two ways to walk an item, each an instantiation of the tile walk below:
+  //  - range (list = std::false_type): the visible keys are exactly
+  //    [key_lo, key_hi) (no mask, or padding only before and after them); position u
+  //    is key tile toff + u and the hidden keys of a tile follow from key_lo, key_hi
+  //    by scalar arithmetic, with no mask reads in the loop;
+  //  - list (std::true_type): any other mask. Position u is entry u of the
+  //    item's tile list (lds_tl; or key tile u for an item longer than the
+  //    list holds), each wave keeps the tiles at positions t .. t + 3 in
+  //    lanes 0 .. 3 of one register (t: the tile the next V step handles; a
+  //    vector register, as the scalar ones are nearly all in use), and every
+  //    tile's mask bytes are read.
+  int toff = 0, key_lo = 0, key_hi = 0;
+  bool use_list = false, list_identity = false;
   int ringv = 0;
-  auto ring_load = [&](int t0) -> int { return (int)lds_tl[min(t0 + (lane & 3), kTileListMax + 7)]; };
+  auto ring_load = [&](int t0) -> int {
+    const int u = t0 + (lane & 3);
+    return list_identity ? u : (int)lds_tl[min(u, kTileListMax + 7)];
+  };
   // key tile at walk position t + k (k = 0 .. 3) while position t is the next V step's
   auto tile_at = [&](int t, int k, auto list) __attribute__((always_inline)) -> int {
     if constexpr (decltype(list)::value) return __builtin_amdgcn_readlane(ringv, k);
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sc[kb] = acc[kb];
-    if (PADMASK) {
+    if constexpr (PADMASK && decltype(list)::value) {
       const int key = tile_at(t, 0, list) * BC + lane;
       mbyte = key < s_kc ? (uint32_t)mg[key] : 1u;
     }
@@ -423,11 +429,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     const int j0 = tile_at(t, 0, list) * BC;
     // hidden-key bits of the tile (padding, keys past s_k); wave-uniform
     uint64_t hid;
-    if (PADMASK) {
+    if constexpr (PADMASK && LIST) {
       hid = __ballot(mbyte != 0u);
     } else {
-      const int rem = s_kc - j0;
-      hid = rem >= BC ? 0ull : ~((1ull << rem) - 1ull);
+      hid = hidden_outside(j0, key_lo, key_hi);
     }
     if (hid != 0ull || (CAUSAL && k0 + j0 + BC - 1 > qlo)) {
       const int lim = qlo + ln - k0 - j0;  // causal: key offset visible iff <= lim
@@ -449,7 +454,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     // is recomputed. O / l is the same for any reference.
     // Without a padding mask every row sees key 0, so tile 0 is every row's
     // first visible tile and the test needs no vote.
-    if (PADMASK ? (__ballot(m_run == -INFINITY) != 0ull) : (t == 0)) {
+    // (walking a range, every row that sees any key sees key key_lo, in tile 0)
+    if ((PADMASK && LIST) ? (__ballot(m_run == -INFINITY) != 0ull) : (t == 0)) {
       float mx = sc[0][0];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -539,12 +545,18 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     if (CAUSAL) kend = min(kend, cur.q0 + BR - k0);
     const int n_t = kend > 0 ? (kend + BC - 1) / BC : 0;
     toff = 0;
+    key_lo = 0;
+    key_hi = s_kc;
     use_list = false;
+    list_identity = false;
     if (PADMASK && n_t <= LIST_MAX) {
       int contig = 1;
-      n_kv = build_tile_list<BC, NT / 64>(mg, kend, n_t, lds_bits, lds_tl, lds_cnt, &toff, &contig);
-      // contiguous visible tiles are walked as a range, others through the list
+      n_kv = build_tile_list<BC, NT / 64>(mg, kend, n_t, lds_bits, lds_tl, lds_scr, &key_lo, &key_hi, &contig);
       use_list = contig == 0;
+      if (!use_list) {  // visible keys [key_lo, key_hi): walk their tiles as a range
+        toff = key_lo / BC;
+        n_kv = key_hi > key_lo ? (key_hi - 1) / BC - toff + 1 : 0;
+      }
     } else if (PADMASK) {
       // a long item: walk every tile up to the last key that is not padded
       if (tid == 0) lds_last = -1;
@@ -571,6 +583,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       }
       kend = min(kend, last + 1);
       n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
+      use_list = true;
+      list_identity = true;
     } else {
       n_kv = n_t;
     }

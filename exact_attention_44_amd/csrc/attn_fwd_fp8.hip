@@ -121,7 +121,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   // the list holds walk every tile up to the last unpadded key.
   __shared__ uint16_t lds_tl[PADMASK ? kTileListMax + 8 : 1];
   __shared__ __attribute__((aligned(8))) uint8_t lds_bits[PADMASK ? kTileListMax / 8 : 8];
-  __shared__ int lds_cnt[3];
+  __shared__ int lds_scr[3 * (NT / 64) + 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -189,17 +189,19 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   float xw[KB][16];        // float32 weights of the tile between its two steps
   i32x8_t pf;              // the same rounded to E4M3 (value product operand)
   uint32_t mbyte = 1u;
-  // Walk position u of the current item is key tile toff + u, unless the
-  // item's visible tiles are not contiguous: then it walks its tile list
-  // (lds_tl), the tile walk is instantiated for that case separately (list =
-  // std::true_type), and each wave keeps the tiles at positions t .. t + 3 in
-  // lanes 0 .. 3 of one register (t: the tile the next V step handles; one
-  // vector register, as the scalar ones are nearly all in use). The
-  // contiguous case keeps the loop free of the list's reads.
-  int toff = 0;
-  bool use_list = false;
+  // Two ways to walk an item, as in the bf16 kernel (each an instantiation of
+  // the tile walk): range (the visible keys are exactly [key_lo, key_hi); position u
+  // is key tile toff + u; hidden keys by scalar arithmetic, no mask reads) and
+  // list (any other mask: position u is entry u of the tile list, or key
+  // tile u past the list's length; a four-entry tile ring in one vector
+  // register; each tile's mask bytes are read).
+  int toff = 0, key_lo = 0, key_hi = 0;
+  bool use_list = false, list_identity = false;
   int ringv = 0;
-  auto ring_load = [&](int t0) -> int { return (int)lds_tl[min(t0 + (lane & 3), kTileListMax + 7)]; };
+  auto ring_load = [&](int t0) -> int {
+    const int u = t0 + (lane & 3);
+    return list_identity ? u : (int)lds_tl[min(u, kTileListMax + 7)];
+  };
   // key tile at walk position t + k (k = 0 .. 3) while position t is the next V step's
   auto tile_at = [&](int t, int k, auto list) __attribute__((always_inline)) -> int {
     if constexpr (decltype(list)::value) return __builtin_amdgcn_readlane(ringv, k);
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
       for (int kb = 0; kb < KB; ++kb) acc[kb] = mfma_e4m3(ka[kb][kk], qf[kk], kk ? acc[kb] : f32x16_t{});
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sc[kb] = acc[kb];
-    if (PADMASK) {
+    if constexpr (PADMASK && decltype(list)::value) {
       const int key = tile_at(t, 0, list) * BC + lane;
       mbyte = key < s_k ? (uint32_t)mg[key] : 1u;
     }
@@ -373,11 +375,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     dma_v(t + 2, tile_at(t, 2, list));
     const int j0 = tile_at(t, 0, list) * BC;
     uint64_t hid;
-    if (PADMASK) {
+    if constexpr (PADMASK && LIST) {
       hid = __ballot(mbyte != 0u);
     } else {
-      const int rem = s_k - j0;
-      hid = rem >= BC ? 0ull : ~((1ull << rem) - 1ull);
+      hid = hidden_outside(j0, key_lo, key_hi);
     }
     if (hid != 0ull || (CAUSAL && j0 + BC - 1 > qlo)) {
       // register r of block kb holds key offset 32 kb + 8 (r / 4) + 4 hl + r % 4
@@ -394,7 +395,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
         }
       }
     }
-    if (PADMASK ? (__ballot(m_run == -INFINITY) != 0ull) : (t == 0)) {
+    // (walking a range, every row that sees any key sees key key_lo, in tile 0)
+    if ((PADMASK && LIST) ? (__ballot(m_run == -INFINITY) != 0ull) : (t == 0)) {
       float mx = sc[0][0];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -440,12 +442,18 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     if (CAUSAL) kend = min(kend, q0 + BR);
     const int n_t = kend > 0 ? (kend + BC - 1) / BC : 0;
     toff = 0;
+    key_lo = 0;
+    key_hi = s_k;
     use_list = false;
+    list_identity = false;
     if (PADMASK && n_t <= kTileListMax) {
       int contig = 1;
-      n_kv = build_tile_list<BC, NT / 64>(mg, kend, n_t, lds_bits, lds_tl, lds_cnt, &toff, &contig);
-      // contiguous visible tiles are walked as a range, others through the list
+      n_kv = build_tile_list<BC, NT / 64>(mg, kend, n_t, lds_bits, lds_tl, lds_scr, &key_lo, &key_hi, &contig);
       use_list = contig == 0;
+      if (!use_list) {  // visible keys [key_lo, key_hi): walk their tiles as a range
+        toff = key_lo / BC;
+        n_kv = key_hi > key_lo ? (key_hi - 1) / BC - toff + 1 : 0;
+      }
     } else if (PADMASK) {
       // a long item: walk every tile up to the last key that is not padded
       if (tid == 0) lds_last = -1;
@@ -472,6 +480,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
       }
       kend = min(kend, last + 1);
       n_kv = kend > 0 ? (kend + BC - 1) / BC : 0;
+      use_list = true;
+      list_identity = true;
     } else {
       n_kv = n_t;
     }
