@@ -78,6 +78,17 @@ MEASURED_TRAFFIC = {
             "lds_instructions_per_wave_tile": 48,
         },
     },
+    "B=4,H=16,s=2048,d=64,key-padding": {
+        "source_sha256": "f54c49f69df29b879ac122c99dd235f79363d6951ba6334a280ff6c24b735478",
+        "fetch_bytes": 63135485,
+        "write_bytes": 17301504,
+        "counters": {
+            "mfma_busy_frac": 0.326,
+            "sustained_clock_ghz": 2.29,
+            "lds_bank_conflicts": 0,
+            "lds_instructions_per_wave_tile": 18.5,
+        },
+    },
     "fp8:B=1,H=32,s=8192,d=128,causal": {
         "source_sha256": "efb8bc8111077fc5686f29e33a9e87e98da2ec2c20568124294c45176e97e9e6",
         "fetch_bytes": 202776791,

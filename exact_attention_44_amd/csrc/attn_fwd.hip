@@ -99,7 +99,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // data, and a padding slot receives its row's first 16 bytes. With VDMA,
   // V's half is 32 rows of RB / 16 slots, written by V_DMA instructions of
   // 64 consecutive slots (a padding slot receives its row's first 16 bytes);
-  // otherwise V goes through registers in items of 2 keys x 8 columns,
+  // otherwise V goes through registers in items of 2 keys x 4 columns (one
+  // per thread of the group, so every wave stages an equal share),
   // transposed on the way into LDS.
   constexpr int GT = NT / 2;
   constexpr int ROW_SLOTS = KS / 16;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int V_DMA = V_SLOTS / 64;
   constexpr int V_DMA_W = (V_DMA + 3) / 4;  // per wave, at most
   static_assert(V_DMA * 64 == V_SLOTS, "a V half tile is a whole number of DMA instructions");
-  constexpr int V_ITEMS = 16 * (D / 8);
+  constexpr int V_ITEMS = 16 * (D / 4);
   constexpr int V_LD = (V_ITEMS + GT - 1) / GT;
   constexpr float kSumLimit = 1048576.f;  // 2^20: see the V step
 
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   };
   // V through registers (not VDMA): load_v(u) fetches this thread's item of
   // tile u of cur (zeros past its end), store_v(u) writes it transposed.
-  u32x4_t vr[V_LD][2];
+  u32x2_t vr[V_LD][2];
   auto load_v = [&](int ti) {
     const int j0 = ti * BC;
     const uint32_t rest = (uint32_t)max(s_kc - j0, 0) * D * 2;
@@ -272,7 +273,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
         const int kq = id & 15, dc = id >> 4;
         const int key = 32 * grp + 2 * kq;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) vr[i][r] = load16(rvt, (uint32_t)((key + r) * D + 8 * dc) * 2);
+        for (int r = 0; r < 2; ++r)
+          vr[i][r] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rvt, (int)(((key + r) * D + 4 * dc) * 2), 0, 0));
       }
     }
   };
@@ -283,9 +285,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       const int id = i * GT + gt;
       if ((V_ITEMS % GT) == 0 || id < V_ITEMS) {
         const int kq = id & 15, dc = id >> 4;
-        char* dst = vl + (8 * dc) * VS + (32 * grp + 2 * kq) * 2;
+        char* dst = vl + (4 * dc) * VS + (32 * grp + 2 * kq) * 2;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < 4; ++c) {
           const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
           *(uint32_t*)(dst + c * VS) = __builtin_amdgcn_perm(vr[i][1][c >> 1], vr[i][0][c >> 1], sel);
         }
