@@ -19,7 +19,9 @@
 //   dkv kernel  one workgroup per (b, h, 128-key tile), 4 waves of 32 keys;
 //               walks the query tiles: S = Q K^T and dP = dO V^T (the key side
 //               stays in registers, one key per lane), dS, then
-//               dV^T += dO^T P and dK^T += Q^T dS.
+//               dV^T += dO^T P and dK^T += Q^T dS. At d = 128 its wave-pair
+//               form runs instead: 8 waves, the two of a SIMD sharing 32 keys,
+//               one computing S, P and dV, the other dP, dS and dK.
 // In both, the rows of the LDS operand are read in the permuted order of
 // key_of_row, so the 32x32 accumulators are the bf16 operands of the next
 // product after a conversion, with no shuffles. The tiles that walk (K and V
@@ -595,6 +597,337 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_bwd_dkv_kernel(BwdP
   }
 }
 
+// ---------------------------------------------------------------------------
+// dkv kernel, wave-pair form
+// ---------------------------------------------------------------------------
+// The same work as attn_bwd_dkv_kernel (one workgroup per (b, h, 128-key
+// tile), walking its 128-query tiles), split between two waves per 32 keys.
+// The single-wave form keeps K and V fragments and both accumulators of its
+// keys, about 430 registers, so one wave runs per SIMD and its vector work
+// adds to its matrix time. Here waves w and w + 4 (which share a SIMD) own
+// keys 32 w .. +31 of the tile:
+//   score side (w):        K fragments; S = Q K^T, P = exp2(S c - lse log2 e)
+//                          with the masks, dV^T += dO^T P;
+//   gradient side (w + 4): V fragments; dP = dO V^T, dS = P (dP - D) with P
+//                          taken from the partner through LDS, dK^T += Q^T dS.
+// Each wave holds one fragment set and one accumulator, so two fit a SIMD
+// and one's vector work overlaps the other's matrix products. P crosses in
+// bf16, the value the dV product uses too. Phase j (closed by a workgroup
+// barrier): the score side handles 32-query block j and writes its P to
+// exchange slot j % 2; the gradient side forms dS and dK of block j - 1 from
+// slot (j - 1) % 2, then dP of block j (kept in registers for the next
+// phase). A slot is written in phase j and read in phase j + 1, and the read
+// of phase j + 1 precedes the next write of the slot (phase j + 2) by a
+// barrier.
+template <int D, bool CAUSAL, bool PADMASK>
+__global__ __launch_bounds__(512, 2) void attn_bwd_dkv_pair_kernel(BwdParams p) {
+  constexpr int NT = 512, BK = 128, BQ = 128;
+  constexpr int QB = BQ / 32, DK = D / 16, DB = D / 32;
+  constexpr int RB = 2 * D;                   // bytes per Q / dO row in LDS
+  constexpr int SL = D / 8;                   // 16-byte slots per row
+  constexpr int TILE = BQ * RB;               // one Q or dO tile
+  constexpr int BUF = 2 * TILE + 2 * BQ * 4;  // Q, dO, lse*log2e, D
+  constexpr int NQ = BQ * SL / NT;            // loads per wave per Q or dO tile
+  constexpr int XS = 4 * 64 * 32;             // exchange slot: 4 wave pairs x 64 lanes x 32 bytes
+  static_assert((BQ * SL) % NT == 0, "a tile is a whole number of loads per wave");
+  static_assert(QB >= 2, "the next tile's loads start in a tile's second block");
+
+  __shared__ __attribute__((aligned(16))) char lds[2 * BUF + 2 * XS];
+  char* const xs = lds + 2 * BUF;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pr = wv & 3;       // wave pair: keys 32 pr .. +31 of the tile
+  const bool grad = wv >= 4;   // gradient side (dP, dS, dK) or score side (S, P, dV)
+  const int hl = lane >> 5, ln = lane & 31;
+  const int L = blockIdx.x;
+  const int kt = L / p.BH;
+  const int bh = L % p.BH, b = bh / p.H;
+  const int k0 = kt * BK;
+  const int s_q = p.s_q, s_k = p.s_k;
+
+  // key side, one key per lane: K (score side) or V (gradient side) fragments
+  const int key = k0 + 32 * pr + ln;
+  bf16x8_t kvf[DK];
+  {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((grad ? p.v : p.k) + (int64_t)bh * s_k * D, (uint32_t)s_k * D * 2);
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+      kvf[kk] = __builtin_bit_cast(bf16x8_t, load16(r, (uint32_t)(key * D + 16 * kk + 8 * hl) * 2));
+  }
+  bool kvis = key < s_k;
+  if (PADMASK && kvis) kvis = p.kpm[(int64_t)b * s_k + key] == 0;
+  // causal: this key is hidden from query qi when kcut > qi (every query
+  // when the key itself is hidden)
+  const int kcut = kvis ? key : INT_MAX;
+  const bool keys_masked = PADMASK || __ballot(!kvis) != 0ull;
+  const int kmax = k0 + 32 * pr + 31;  // the pair's last key
+
+  // query tiles that can see a key of this tile; none when every key of the
+  // block is padded (its gradients are zero)
+  const int qt0 = CAUSAL ? min(k0, s_q) / BQ : 0;
+  int qt1 = (s_q + BQ - 1) / BQ;
+  if (PADMASK && !__syncthreads_or(kvis)) qt1 = qt0;
+  const uint16_t* qg = p.q + (int64_t)bh * s_q * D;
+  const uint16_t* dg = p.dout + (int64_t)bh * s_q * D;
+  const float* l2g = p.lse2w + (int64_t)bh * p.s_qp;
+  const float* Dg = p.delta + (int64_t)bh * p.s_qp;
+
+  // Staging: loads that write LDS directly, untracked by the compiler (it
+  // would otherwise wait for them before the next LDS read of any buffer);
+  // the barrier before a tile's first use waits for them. Load i of this
+  // wave fills LDS slots 64 (8 i + wv) .. +63 of the Q and of the dO tile.
+  // Rows past s_q read zeros.
+  uint32_t q_voff[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int sl = 64 * (8 * i + wv) + lane;
+    const int r = sl / SL, ph = sl % SL;
+    q_voff[i] = (uint32_t)(r * RB + 16 * (ph ^ q_swz<D>(r)));
+  }
+  auto dma_tile = [&](int u, int bi) __attribute__((always_inline)) {
+    const int i0 = u * BQ;
+    char* base = lds + bi * BUF;
+    const uint32_t rest = (uint32_t)max(s_q - i0, 0) * RB;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+      load16_to_lds_untracked(qg + (int64_t)i0 * D, rest, base + 64 * (8 * i + wv) * 16, q_voff[i]);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+      load16_to_lds_untracked(dg + (int64_t)i0 * D, rest, base + TILE + 64 * (8 * i + wv) * 16, q_voff[i]);
+    // lse*log2e then D of the tile's BQ rows, BQ / 4 slots each: wave wv < 4
+    // loads slots LS (wv & 1) .. +LS-1 of lse*log2e (waves 0, 1) or of D
+    // (waves 2, 3). The workspace holds s_qp >= i0 + BQ rows per (b, h).
+    constexpr int LS = BQ / 8;
+    if (wv < 4 && lane < LS)
+      load16_to_lds_untracked((wv < 2 ? l2g : Dg) + i0, BQ * 4, base + 2 * TILE + 16 * LS * wv,
+                              (uint32_t)(16 * (LS * (wv & 1) + lane)));
+  };
+
+  // Score-side fragment reads (Q for S, dO for dP): lane (ln, hl) reads row
+  // key_of_row(ln) of each 32-row block at logical slot 2 kk + hl.
+  int a_off[DK];
+  {
+    const int r = key_of_row(ln);
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) a_off[kk] = r * RB + 16 * ((2 * kk + hl) ^ q_swz<D>(r));
+  }
+  // Transpose reads of the gradient products' A operands (dO^T for dV, Q^T
+  // for dK), as in the single-wave form.
+  int t_off[2][DB];
+  {
+    const int a = lane & 15, g = (lane >> 4) & 1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = 8 * hl + 4 * r + (a >> 2);
+        const int slot = 4 * db + 2 * g + ((a & 3) >> 1);
+        t_off[r][db] = row * RB + 16 * (slot ^ q_swz<D>(row)) + 8 * (a & 1);
+      }
+  }
+  // this lane's 32 bytes of a P block in an exchange slot (16 per half)
+  const int x_off = pr * 2048 + lane * 16;
+
+  f32x16_t acc[DB];  // dV^T (score side) or dK^T (gradient side)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
+  f32x16_t dpk = {};  // gradient side: dP of the block whose dS comes next
+
+  // the gradient product of one block: acc[db] += A^T (rows of the block) x w,
+  // A^T from transpose reads of the block's rows (grad_reads)
+  auto grad_reads = [&](const char* src, int qb, u32x2_t (&t)[2][DB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) t[ks][db][r] = lds_read_tr16(src + t_off[r][db] + (32 * qb + 16 * ks) * RB);
+  };
+  auto grad_mfma = [&](const u32x2_t (&t)[2][DB][2], const bf16x8_t* w) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x4_t a = {t[ks][db][0][0], t[ks][db][0][1], t[ks][db][1][0], t[ks][db][1][1]};
+        acc[db] = mfma(__builtin_bit_cast(bf16x8_t, a), w[ks], acc[db]);
+      }
+  };
+  // S (score side) or dP (gradient side) of one block: one key per lane, the
+  // registers hold queries 32 qb + {8 hl .. 8 hl + 7, 16 + 8 hl .. +7}
+  auto score_reads = [&](const char* src, int qb, bf16x8_t (&f)[DK]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) f[kk] = *(const bf16x8_t*)(src + a_off[kk] + qb * 32 * RB);
+  };
+  auto score_mfma = [&](const bf16x8_t (&f)[DK]) __attribute__((always_inline)) -> f32x16_t {
+    f32x16_t s = {};
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) s = mfma(f[kk], kvf[kk], s);
+    return s;
+  };
+  // The barrier closing a phase, without the wait of a fenced barrier for
+  // every LDS access of the wave: the reads of the next phase's operands stay
+  // in flight across it (they read a tile that no wave writes before two
+  // more barriers have passed). The only LDS writes of a phase, the score
+  // side's P, are waited for explicitly before it; the memory clobber keeps
+  // the compiler from moving LDS accesses across it.
+  auto phase_sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int n_it = qt1 - qt0;
+  const int nb = n_it * QB;  // 32-query blocks
+  if (n_it > 0) dma_tile(qt0, 0);
+  wait_loads();
+  __syncthreads();
+  // Each side runs its own loop over the phases (one loop with a branch per
+  // side made the compiler copy the accumulators at the join every phase);
+  // both take the same barriers.
+  auto phase_begin = [&](int j) __attribute__((always_inline)) {
+    // the next tile goes to the other buffer once its last reader, the
+    // gradient side's block before this tile, has passed a barrier
+    const int it = j / QB;
+    if (j % QB == 1 && it + 1 < n_it) dma_tile(qt0 + it + 1, (it + 1) & 1);
+  };
+  auto phase_end = [&](int j) __attribute__((always_inline)) {
+    // the next tile's loads have landed before the barrier that precedes its
+    // first block
+    if (j % QB == QB - 1 && j / QB + 1 < n_it) wait_loads();
+    phase_sync();
+  };
+  // Software pipelining across the barriers: each side requests the LDS
+  // operands of its next phase at the end of the current one (after the
+  // products that consume the registers), so their latency overlaps the
+  // barrier and the other waves' work. A block that starts a new tile is
+  // read after the barrier that makes the tile valid; so is P, which the
+  // partner writes in the phase before.
+  if (!grad) {
+    f32x4_t lv[4];           // lse*log2e of the block's rows
+    bf16x8_t f[DK];          // Q fragments (S)
+    u32x2_t t[2][DB][2];     // dO^T (dV)
+    auto loads = [&](int j) __attribute__((always_inline)) {
+      const int it = j / QB, qb = j % QB;
+      const char* ql = lds + (it & 1) * BUF;
+      const float* lw = (const float*)(ql + 2 * TILE);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int qo = 32 * qb + 16 * h2 + 8 * hl;
+        lv[2 * h2] = *(const f32x4_t*)(lw + qo);
+        lv[2 * h2 + 1] = *(const f32x4_t*)(lw + qo + 4);
+      }
+      score_reads(ql, qb, f);
+      grad_reads(ql + TILE, qb, t);
+    };
+    for (int j = 0; j <= nb; ++j) {
+      phase_begin(j);
+      if (j < nb) {
+        const int it = j / QB, qb = j % QB;
+        if (qb == 0) loads(j);
+        __builtin_amdgcn_sched_barrier(0);
+        const int qrow = (qt0 + it) * BQ + 32 * qb;
+        const f32x16_t s = score_mfma(f);
+        float pw[16];
+        // masks where a key is hidden, on the causal diagonal, and on the
+        // ragged last block (its rows past s_q carry lse = -inf)
+        if (keys_masked || (CAUSAL && qrow < kmax) || qrow + 32 > s_q) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float lr = lv[r >> 2][r & 3];
+            const int qi = qrow + 16 * (r >> 3) + 8 * hl + (r & 7);
+            const bool hide = (lr == -INFINITY) | (CAUSAL ? (kcut > qi) : !kvis);
+            pw[r] = __builtin_amdgcn_exp2f(hide ? -INFINITY : fmaf(s[r], p.c, -lr));
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pw[r] = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -lv[r >> 2][r & 3]));
+        }
+        bf16x8_t pp[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4_t w;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) w[e2] = pack_bf16(pw[8 * ks + 2 * e2], pw[8 * ks + 2 * e2 + 1]);
+          pp[ks] = __builtin_bit_cast(bf16x8_t, w);
+          *(u32x4_t*)(xs + (j & 1) * XS + x_off + 1024 * ks) = w;
+        }
+        grad_mfma(t, pp);  // dV^T += dO^T P
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P is in LDS before the barrier
+        if (qb + 1 < QB && j + 1 < nb) loads(j + 1);
+      }
+      phase_end(j);
+    }
+  } else {
+    f32x4_t dv4[4];          // D of the rows of the block whose dS comes next
+    u32x2_t t[2][DB][2];     // Q^T of that block (dK)
+    bf16x8_t fn[DK];         // dO fragments of the block whose dP comes next
+    auto dO_loads = [&](int j) __attribute__((always_inline)) {
+      score_reads(lds + ((j / QB) & 1) * BUF + TILE, j % QB, fn);
+    };
+    for (int j = 0; j <= nb; ++j) {
+      phase_begin(j);
+      if (j < nb && j % QB == 0) dO_loads(j);
+      if (j > 0) {
+        const int jb = j - 1;
+        u32x4_t pw[2];  // P of block jb, from the partner
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) pw[ks] = *(const u32x4_t*)(xs + (jb & 1) * XS + x_off + 1024 * ks);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8_t pd[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4_t w;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const int r = 8 * ks + 2 * e2;
+            const float p0 = __builtin_bit_cast(float, pw[ks][e2] << 16);
+            const float p1 = __builtin_bit_cast(float, pw[ks][e2] & 0xFFFF0000u);
+            w[e2] = pack_bf16(p0 * (dpk[r] - dv4[r >> 2][r & 3]), p1 * (dpk[r + 1] - dv4[(r + 1) >> 2][(r + 1) & 3]));
+          }
+          pd[ks] = __builtin_bit_cast(bf16x8_t, w);
+        }
+        grad_mfma(t, pd);  // dK^T += Q^T dS
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j < nb) {
+        dpk = score_mfma(fn);  // dP = dO V^T
+        __builtin_amdgcn_sched_barrier(0);
+        // operands of the next phase: D and Q^T of this block (its dS and
+        // dK come next), dO of the next block when it is in this tile
+        const int it = j / QB, qb = j % QB;
+        const char* ql = lds + (it & 1) * BUF;
+        const float* lw = (const float*)(ql + 2 * TILE);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int qo = BQ + 32 * qb + 16 * h2 + 8 * hl;
+          dv4[2 * h2] = *(const f32x4_t*)(lw + qo);
+          dv4[2 * h2 + 1] = *(const f32x4_t*)(lw + qo + 4);
+        }
+        grad_reads(ql, qb, t);
+        if (qb + 1 < QB && j + 1 < nb) dO_loads(j + 1);
+      }
+      phase_end(j);
+    }
+  }
+
+  if (key < s_k) {
+    uint16_t* g = (grad ? p.dk : p.dv) + ((int64_t)bh * s_k + key) * D;
+    const float f = grad ? p.scale : 1.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        u32x2_t w;
+        w[0] = pack_bf16(acc[db][4 * gi + 0] * f, acc[db][4 * gi + 1] * f);
+        w[1] = pack_bf16(acc[db][4 * gi + 2] * f, acc[db][4 * gi + 3] * f);
+        *(u32x2_t*)(g + 32 * db + 8 * gi + 4 * hl) = w;
+      }
+  }
+}
+
 // Zero n 16-bit elements (a degenerate problem's gradients). A kernel rather
 // than a memset, so the call can be captured into a graph.
 __global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* p, int64_t n) {
@@ -613,8 +946,12 @@ hipError_t launch_bwd(const BwdParams& p, int grid_q, int grid_k, hipStream_t s)
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, PADMASK>), dim3(grid_q), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (grid_k > 0)
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, CAUSAL, PADMASK>), dim3(grid_k), dim3(256), 0, s, p);
+  if (grid_k > 0) {
+    if constexpr (D == 128)
+      hipLaunchKernelGGL((attn_bwd_dkv_pair_kernel<D, CAUSAL, PADMASK>), dim3(grid_k), dim3(512), 0, s, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, CAUSAL, PADMASK>), dim3(grid_k), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
