@@ -35,6 +35,7 @@ and on the padded d = 64 one (`other_workloads`; --no-other-workloads skips
 them, as the profiler commands do).
 """
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -60,26 +61,39 @@ KERNEL_SOURCE_FP8 = os.path.join(ROOT, "exact_attention_44_amd", "csrc", "attn_f
 # WRITE_SIZE) of this script, each scaled by what the same counter reports for
 # a 1 GiB copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the mean over the
 # launches after the first (the first runs with cold caches, the timed
-# launches run back to back). Valid only for the kernel source they were taken
-# on: reported as null once the source's hash differs.
+# launches run back to back). Valid only for the kernel code they were taken
+# on: reported as null once the code's hash (code_sha256: the source without
+# its // comments and blank lines) differs.
+def code_sha256(path: str) -> str:
+    """sha256 of a C++/HIP source with its // comments, trailing blanks and
+    blank lines removed: a comment-only edit keeps the hash."""
+    lines = []
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 MEASURED_TRAFFIC = {
     "B=1,H=32,s=8192,d=128,causal": {
-        "source_sha256": "a7d8f64b8e2a1b75c1b7f33b6811282ce799a7c3ee0513406f9068b91f819946",
-        "fetch_bytes": 502197043,
-        "write_bytes": 68157909,
+        "code_sha256": "69147dfccd582324d16eb44d96ec2a1234c39c855e88391939728eca8b6e21a1",
+        "fetch_bytes": 478404744,
+        "write_bytes": 68157440,
         # SQ counter passes of the same command (mean over the launches after
         # the first): MFMA-busy cycles per SIMD over SQ busy cycles per shader
         # engine (32 engines), the clock those busy cycles imply over the
         # launch, LDS bank conflicts, LDS instructions per wave and 64-key tile
         "counters": {
-            "mfma_busy_frac": 0.695,
-            "sustained_clock_ghz": 1.54,
+            "mfma_busy_frac": 0.689,
+            "sustained_clock_ghz": 1.70,
             "lds_bank_conflicts": 0,
             "lds_instructions_per_wave_tile": 48,
         },
     },
     "B=4,H=16,s=2048,d=64,key-padding": {
-        "source_sha256": "f54c49f69df29b879ac122c99dd235f79363d6951ba6334a280ff6c24b735478",
+        "code_sha256": "69147dfccd582324d16eb44d96ec2a1234c39c855e88391939728eca8b6e21a1",
         "fetch_bytes": 63135485,
         "write_bytes": 17301504,
         "counters": {
@@ -90,7 +104,7 @@ MEASURED_TRAFFIC = {
         },
     },
     "fp8:B=1,H=32,s=8192,d=128,causal": {
-        "source_sha256": "efb8bc8111077fc5686f29e33a9e87e98da2ec2c20568124294c45176e97e9e6",
+        "code_sha256": "62660c610cc147c9c5ab7d0f544fbe508a430846cf99eab0ef72d21e952dfda7",
         "fetch_bytes": 202776791,
         "write_bytes": 68177216,
     },
@@ -397,14 +411,12 @@ def main():
     measured = None if (a.backward or split or a.unfused) else \
         MEASURED_TRAFFIC.get(("fp8:" if a.fp8 else "") + w.name)
     if measured is not None:
-        import hashlib
-        with open(KERNEL_SOURCE_FP8 if a.fp8 else KERNEL_SOURCE, "rb") as f:
-            current = hashlib.sha256(f.read()).hexdigest()
-        if current == measured["source_sha256"]:
+        current = code_sha256(KERNEL_SOURCE_FP8 if a.fp8 else KERNEL_SOURCE)
+        if current == measured["code_sha256"]:
             traffic = measured["fetch_bytes"] + measured["write_bytes"]
             traffic_detail.update(fetch_bytes=measured["fetch_bytes"],
                                   write_bytes=measured["write_bytes"],
-                                  source_sha256=current)
+                                  code_sha256=current)
             if "counters" in measured:
                 traffic_detail["counters"] = measured["counters"]
     value = flops * a.steps / wall / 1e12
@@ -438,7 +450,8 @@ def main():
             "traffic_unit": "bytes per launch",
             "traffic_detail": traffic_detail,
             "kernel": ("attn_fwd_fp8_kernel" if a.fp8
-                       else "attn_bwd_dq_kernel + attn_bwd_dkv_kernel" if a.backward
+                       else ("attn_bwd_dq_kernel + " + ("attn_bwd_dkv_pair_kernel" if w.d == 128
+                                                         else "attn_bwd_dkv_kernel")) if a.backward
                        else "attn_fwd_kernel (key-split) + attn_merge_kernel" if split
                        else "attn_fwd_kernel"),
             "kernel_avg_ms": round(kern_avg_ms, 5),

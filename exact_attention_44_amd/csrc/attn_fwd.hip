@@ -140,8 +140,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // ---- work items. Item L is (key chunk, query tile, (b, h)) with the
   // (b, h) index fastest, so when B*H is a multiple of 8 every item of a head
   // has the same L mod 8 (the device deals workgroups to its 8 XCDs
-  // round-robin, so a head's items share an XCD's L2); causal launches take
-  // the longest query tiles first. At D = 128 each workgroup takes one item
+  // round-robin, so all of a head's items run on one XCD; an XCD runs 32
+  // workgroups at a time, from several heads whose K and V need not fit its
+  // L2, and misses are served from the MALL: an order of one head per XCD at
+  // a time re-read less but ran slower); causal launches take the longest
+  // query tiles first. At D = 128 each workgroup takes one item
   // (L = its index). At D = 64 the grid is persistent (at most one workgroup
   // per CU), which saves the start and end of a workgroup per item (measured
   // +8 % on the padded workload; at D = 128 the loop over items made the
