@@ -26,9 +26,10 @@
 // lane too, so the rescale by exp(m_old - m_new) is a per-lane scalar.
 //
 // LDS: K tile row-major [BC][D] with rows padded by 16 bytes, so every
-// 16-lane fragment read hits distinct banks, loaded from memory straight into
-// LDS (buffer loads with LDS as the destination). At D = 128 the V tile is
-// loaded the same way, row-major [BC][D] with rows padded by 64 bytes, and
+// 16-lane fragment read hits distinct banks; at D = 128 loaded from memory
+// straight into LDS (buffer loads with LDS as the destination), at D = 64
+// through registers (a 16-byte unit per thread). At D = 128 the V tile is
+// loaded straight into LDS too, row-major [BC][D] with rows padded by 64 bytes, and
 // read as the transposed operand V^T by 16-bit LDS transpose reads (the
 // padding puts the four rows each half wave reads on disjoint banks, and
 // keeps every lane's read addresses one base plus compile-time offsets). At D = 64 the V tile passes through registers
@@ -91,17 +92,17 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int K_BYTES = BC * KS;
   constexpr int BUF_BYTES = K_BYTES + (VDMA ? BC * RB : D * VS);
   constexpr int NBUF = 4;             // see the schedule below
-  // Each group stages its half (32 keys) of a tile. K goes from memory
-  // straight into its padded LDS rows (buffer loads with LDS as the
+  // Each group stages its half (32 keys) of a tile. With VDMA, K goes from
+  // memory straight into its padded LDS rows (buffer loads with LDS as the
   // destination): the half is 32 rows of ROW_SLOTS 16-byte slots, written by
   // K_DMA instructions of 64 consecutive slots each; the last instruction
   // overlaps its predecessor, so the overlap is written twice with the same
   // data, and a padding slot receives its row's first 16 bytes. With VDMA,
   // V's half is 32 rows of RB / 16 slots, written by V_DMA instructions of
   // 64 consecutive slots (a padding slot receives its row's first 16 bytes);
-  // otherwise V goes through registers in items of 2 keys x 4 columns (one
-  // per thread of the group, so every wave stages an equal share),
-  // transposed on the way into LDS.
+  // otherwise K and V go through registers: K in one 16-byte unit per thread
+  // of the group, V in items of 2 keys x 4 columns (one per thread, so every
+  // wave stages an equal share), transposed on the way into LDS.
   constexpr int GT = NT / 2;
   constexpr int ROW_SLOTS = KS / 16;
   constexpr int K_SLOTS = 32 * ROW_SLOTS;
@@ -215,8 +216,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     const int row = 32 * grp + slot / ROW_SLOTS, un = slot % ROW_SLOTS;
     k_voff[i] = (uint32_t)(row * D + (un < KU ? 8 * un : 0)) * 2;
   }
-  // K rows of tile u into LDS; completes asynchronously (the next fenced
-  // barrier of this wave waits for it).
+  // VDMA: K rows of tile u into LDS; completes asynchronously (the next
+  // fenced barrier of this wave waits for it).
   // The tile at walk position u of cur is key tile ti (keys ti * BC ..; ti
   // == u except where a padding mask skips tiles); nothing past the walk.
   auto src_tile = [&](const uint16_t* base_cur, int u, int ti, const uint16_t*& src, uint32_t& bytes) -> bool {
@@ -280,6 +281,22 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
           vr[i][r] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rvt, (int)(((key + r) * D + 4 * dc) * 2), 0, 0));
       }
     }
+  };
+  // K through registers (not VDMA): each thread of a group holds 16 bytes of
+  // one of the group's 32 key rows; load_k(ti) fetches them from key tile ti
+  // (zeros past its end), store_k(u) writes them to the K rows of tile u.
+  static_assert(VDMA || 32 * KU == GT, "not VDMA: one 16-byte unit of a K half tile per thread");
+  u32x4_t kr;  // the K half tile in flight
+  auto load_k = [&](int ti) __attribute__((always_inline)) -> u32x4_t {
+    const int j0 = ti * BC;
+    const uint32_t rest = (uint32_t)max(s_kc - j0, 0) * D * 2;
+    const __amdgpu_buffer_rsrc_t rkt = make_rsrc(kg + (int64_t)j0 * D, rest);
+    return load16(rkt, (uint32_t)((32 * grp + gt / KU) * D + 8 * (gt % KU)) * 2);
+  };
+  auto store_k = [&](int u, u32x4_t x) __attribute__((always_inline)) {
+    if (u >= n_kv) return;
+    char* kl = lds + ((boff + u) & (NBUF - 1)) * BUF_BYTES;
+    *(u32x4_t*)(kl + (32 * grp + gt / KU) * KS + 16 * (gt % KU)) = x;
   };
   auto store_v = [&](int u) {
     char* vl = lds + ((boff + u) & (NBUF - 1)) * BUF_BYTES + K_BYTES;
@@ -407,6 +424,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     if constexpr (!VDMA) {
       store_v(tq + 1);
       load_v(tile_at(tq, 2, list));
+      // K(u) is read by group 0 from interval u on: both halves are stored
+      // in interval u - 1 (group 0's M(u - 1), group 1's M(u - 2)) and
+      // fetched an interval before that
+      store_k(tq + 1 + grp, kr);
+      kr = load_k(tile_at(tq, 2 + grp, list));
     }
 #pragma unroll
     for (int i = 0; i < N_PV - LA; ++i) {
@@ -429,8 +451,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     // LDS so the compiler has no reason to wait for those loads here
     int ring_new = 0;
     if constexpr (LIST) ring_new = ring_load(t + 1);
-    dma_k(t + 3, tile_at(t, 3, list));
-    if constexpr (VDMA) dma_v(t + 2, tile_at(t, 2, list));
+    if constexpr (VDMA) {
+      dma_k(t + 3, tile_at(t, 3, list));
+      dma_v(t + 2, tile_at(t, 2, list));
+    }
     const int j0 = tile_at(t, 0, list) * BC;
     // hidden-key bits of the tile (padding, keys past s_k); wave-uniform
     uint64_t hid;
@@ -601,13 +625,20 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       return (PADMASK && use_list) ? __builtin_amdgcn_readlane(ringv, k) : toff + k;
     };
     if (n_kv > 0) {
-      dma_k(0, first_tile(0));
-      dma_k(1, first_tile(1));
-      dma_k(2, first_tile(2));
       if constexpr (VDMA) {
+        dma_k(0, first_tile(0));
+        dma_k(1, first_tile(1));
+        dma_k(2, first_tile(2));
         dma_v(0, first_tile(0));
         dma_v(1, first_tile(1));
       } else {
+        // K(0), K(1) (and group 1's half of K(2), which its first interval,
+        // without an M step, cannot store) now; the next K half in flight
+        const u32x4_t k0 = load_k(first_tile(0)), k1 = load_k(first_tile(1)), k2 = load_k(first_tile(2));
+        kr = grp == 1 ? load_k(first_tile(3)) : k2;
+        store_k(0, k0);
+        store_k(1, k1);
+        if (grp == 1) store_k(2, k2);
         load_v(first_tile(0));
         store_v(0);
         load_v(first_tile(1));
@@ -624,8 +655,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     mbyte = 1u;
 
     // ---- ping-pong schedule: n_kv + 2 intervals, each closed by a workgroup
-    // barrier. M(t) = [PV(t-1), QK(t)] issues matrix-core work, V(t) =
-    // [K (and, VDMA, V) staging, softmax of S(t)] vector-ALU work. Interval 0:
+    // barrier. M(t) = [PV(t-1), QK(t)] issues matrix-core work (and, at
+    // D = 64, the register staging of K and V), V(t) = [VDMA: K and V
+    // staging; softmax of S(t)] vector-ALU work. Interval 0:
     // group 0 runs QK(0). Interval t + 1 (t < n_kv): group 0 runs V(t) then
     // M(t + 1), group 1 runs M(t) then V(t) (M(n_kv) is PV(n_kv - 1) alone).
     // Interval n_kv + 1: group 1 runs PV(n_kv - 1). Waves w and w + 4 share a
@@ -633,9 +665,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     // two units overlap; within an interval the two waves switch kinds without
     // a barrier, which saves one barrier per tile over a barrier at every
     // switch.
-    // LDS buffer u % 4 holds tile u. Its K part is written (by load-to-LDS
-    // in V(u - 3)) in interval u - 2 and read by QK(u) in intervals u (group
-    // 0) and u + 1 (group 1). Its V part is written in interval u - 1 (VDMA:
+    // LDS buffer u % 4 holds tile u. Its K part is written in interval u - 2
+    // (VDMA: load-to-LDS in V(u - 3)) or u - 1 (stores in group 0's M(u - 1)
+    // and group 1's M(u - 2), fetched into registers an interval before) and
+    // read by QK(u) in intervals u (group 0) and u + 1 (group 1). Its V part is written in interval u - 1 (VDMA:
     // load-to-LDS in V(u - 2); otherwise stores in M(u - 1), group 0 in
     // interval u - 1 and group 1 in interval u) and read from the prefetch at
     // the end of V(u) (interval u + 1) to PV(u) of group 1 (interval u + 2).
