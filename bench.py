@@ -78,9 +78,9 @@ def code_sha256(path: str) -> str:
 
 MEASURED_TRAFFIC = {
     "B=1,H=32,s=8192,d=128,causal": {
-        "code_sha256": "69147dfccd582324d16eb44d96ec2a1234c39c855e88391939728eca8b6e21a1",
-        "fetch_bytes": 478404744,
-        "write_bytes": 68157440,
+        "code_sha256": "28298fea1f14082d32f1146781266c94cf9132e638f6e1469cd5ec0b300564f7",
+        "fetch_bytes": 479088982,
+        "write_bytes": 68157696,
         # SQ counter passes of the same command (mean over the launches after
         # the first): MFMA-busy cycles per SIMD over SQ busy cycles per shader
         # engine (32 engines), the clock those busy cycles imply over the
@@ -93,8 +93,8 @@ MEASURED_TRAFFIC = {
         },
     },
     "B=4,H=16,s=2048,d=64,key-padding": {
-        "code_sha256": "69147dfccd582324d16eb44d96ec2a1234c39c855e88391939728eca8b6e21a1",
-        "fetch_bytes": 63135485,
+        "code_sha256": "28298fea1f14082d32f1146781266c94cf9132e638f6e1469cd5ec0b300564f7",
+        "fetch_bytes": 64797826,
         "write_bytes": 17301504,
         "counters": {
             "mfma_busy_frac": 0.326,
