@@ -618,8 +618,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       n_kv = n_t;
     }
     load_q(cur);
-    // the first tiles' loads (positions 0 .. 2); selects rather than a branch
-    // on the kind of walk
+    // the first tiles' loads (positions 0 .. 2, and at D = 64 group 1's K of
+    // position 3); selects rather than a branch on the kind of walk
     if (PADMASK) ringv = ring_load(0);
     auto first_tile = [&](int k) -> int {
       return (PADMASK && use_list) ? __builtin_amdgcn_readlane(ringv, k) : toff + k;
