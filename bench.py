@@ -97,16 +97,16 @@ MEASURED_TRAFFIC = {
         "fetch_bytes": 64797826,
         "write_bytes": 17301504,
         "counters": {
-            "mfma_busy_frac": 0.326,
-            "sustained_clock_ghz": 2.29,
+            "mfma_busy_frac": 0.338,
+            "sustained_clock_ghz": 2.17,
             "lds_bank_conflicts": 0,
-            "lds_instructions_per_wave_tile": 18.5,
+            "lds_instructions_per_wave_tile": 19.5,
         },
     },
     "fp8:B=1,H=32,s=8192,d=128,causal": {
-        "code_sha256": "62660c610cc147c9c5ab7d0f544fbe508a430846cf99eab0ef72d21e952dfda7",
-        "fetch_bytes": 202776791,
-        "write_bytes": 68177216,
+        "code_sha256": "e779acb56cc1bc5bf12e27322a1c62441d01eb6b48f0408f96a497cbe5aadf82",
+        "fetch_bytes": 202676833,
+        "write_bytes": 68177931,
     },
 }
 
