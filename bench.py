@@ -111,6 +111,24 @@ MEASURED_TRAFFIC = {
 }
 
 
+def algorithmic_bytes_of(w, mode: str) -> int:
+    """HBM bytes one call must move at least: every input read once and every
+    output written once (for the materialising path, also its score matrix:
+    written, read and rewritten in place, read again, 2 bytes per score each
+    time)."""
+    B, H, s_q, s_k, d = w.B, w.H, w.s_q, w.s_k, w.d
+    out_lse = 2 * B * H * s_q * d + 4 * B * H * s_q
+    if mode == "unfused":
+        return 8 * B * H * s_q * s_k + 2 * B * H * (s_q + 2 * s_k) * d + out_lse
+    if mode == "fp8":  # E4M3 q, k, v (one byte each) and three float32 descales per head
+        return B * H * (s_q + 2 * s_k) * d + 12 * B * H + out_lse
+    if mode == "backward":  # read q, out, dout, k, v, lse; write dq, dk, dv
+        return 2 * B * H * (3 * s_q + 2 * s_k) * d + 4 * B * H * s_q + 2 * B * H * (s_q + 2 * s_k) * d
+    if mode == "forward":
+        return 2 * B * H * (s_q + 2 * s_k) * d + out_lse
+    raise ValueError(mode)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,18 +413,8 @@ def main():
         fused_ms = time_launches(fused_step, stream, a.steps)[0]
 
     flops = w.flops() * (2.5 if a.backward else 1.0)
-    if a.unfused:  # the score matrix written, read and written in place, read again
-        algorithmic_bytes = 8 * w.B * w.H * w.s_q * w.s_k + 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d \
-            + 2 * w.B * w.H * w.s_q * w.d + 4 * w.B * w.H * w.s_q
-    elif a.fp8:  # E4M3 q, k, v (one byte each) and the descales read; bf16 out, lse written
-        algorithmic_bytes = w.B * w.H * (w.s_q + 2 * w.s_k) * w.d + 12 * w.B * w.H \
-            + 2 * w.B * w.H * w.s_q * w.d + 4 * w.B * w.H * w.s_q
-    elif a.backward:  # read q, out, dout, k, v, lse; write dq, dk, dv
-        algorithmic_bytes = 2 * w.B * w.H * (3 * w.s_q + 2 * w.s_k) * w.d + 4 * w.B * w.H * w.s_q \
-            + 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d
-    else:
-        algorithmic_bytes = 2 * w.B * w.H * (w.s_q + 2 * w.s_k) * w.d + 2 * w.B * w.H * w.s_q * w.d \
-            + 4 * w.B * w.H * w.s_q
+    mode = "unfused" if a.unfused else "fp8" if a.fp8 else "backward" if a.backward else "forward"
+    algorithmic_bytes = algorithmic_bytes_of(w, mode)
     traffic, traffic_detail = None, {"algorithmic_bytes": algorithmic_bytes}
     measured = None if (a.backward or split or a.unfused) else \
         MEASURED_TRAFFIC.get(("fp8:" if a.fp8 else "") + w.name)
