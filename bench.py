@@ -103,6 +103,16 @@ MEASURED_TRAFFIC = {
             "lds_instructions_per_wave_tile": 19.5,
         },
     },
+    "B=1,H=32,s=4096,d=128,causal": {
+        "code_sha256": "28298fea1f14082d32f1146781266c94cf9132e638f6e1469cd5ec0b300564f7",
+        "fetch_bytes": 145902421,
+        "write_bytes": 34078720,
+    },
+    "B=1,H=32,s=32768,d=128,causal,Kx3": {
+        "code_sha256": "28298fea1f14082d32f1146781266c94cf9132e638f6e1469cd5ec0b300564f7",
+        "fetch_bytes": 4865809694,
+        "write_bytes": 272635563,
+    },
     "fp8:B=1,H=32,s=8192,d=128,causal": {
         "code_sha256": "e779acb56cc1bc5bf12e27322a1c62441d01eb6b48f0408f96a497cbe5aadf82",
         "fetch_bytes": 202676833,
