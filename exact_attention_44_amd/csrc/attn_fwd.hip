@@ -26,16 +26,17 @@
 // lane too, so the rescale by exp(m_old - m_new) is a per-lane scalar.
 //
 // LDS: K tile row-major [BC][D] with rows padded by 16 bytes, so every
-// 16-lane fragment read hits distinct banks; at D = 128 loaded from memory
-// straight into LDS (buffer loads with LDS as the destination), at D = 64
-// through registers (a 16-byte unit per thread). At D = 128 the V tile is
-// loaded straight into LDS too, row-major [BC][D] with rows padded by 64 bytes, and
+// 16-lane fragment read hits distinct banks; loaded from memory straight into
+// LDS (buffer loads with LDS as the destination). The V tile is loaded
+// straight into LDS too, row-major [BC][D] with rows padded by 64 bytes, and
 // read as the transposed operand V^T by 16-bit LDS transpose reads (the
 // padding puts the four rows each half wave reads on disjoint banks, and
-// keeps every lane's read addresses one base plus compile-time offsets). At D = 64 the V tile passes through registers
-// and is stored transposed, [D][BC] with padded rows, and read by plain
-// fragment reads: the transpose reads, two per fragment, cost more there
-// than the register transpose. Four buffers. The two wave groups take
+// keeps every lane's read addresses one base plus compile-time offsets).
+// At D = 64 with a key-padding mask both tiles pass through registers
+// instead: K a 16-byte unit per thread, V stored transposed, [D][BC] with
+// padded rows, and read by plain fragment reads (measured faster there,
+// while without a mask the loads into LDS are faster). Four buffers. The two
+// wave groups take
 // turns (ping-pong): while one group's waves run the matrix products, the
 // other group's waves run the softmax, and each SIMD holds one wave of each
 // group, because a wave's own vector instructions do not overlap its own
@@ -85,7 +86,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // LDS rows are padded by 16 bytes: with these strides the 16 lanes of every
   // fragment read hit 16 distinct 4-bank groups, and each lane's fragment
   // addresses are one base plus compile-time offsets.
-  constexpr bool VDMA = D == 128;     // V by load-to-LDS and transpose reads
+  // K and V by load-to-LDS, V read by transpose reads; otherwise (D = 64 with
+  // a padding mask) both through registers
+  constexpr bool VDMA = D == 128 || !PADMASK;
   constexpr int KS = D * 2 + 16;      // K row stride (bytes)
   constexpr int RB = D * 2 + 64;      // V row stride with VDMA (bytes)
   constexpr int VS = BC * 2 + 16;     // V^T row stride otherwise (bytes)
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
   // takes one item per round, g in even rounds and the mirror image of g
   // within its round in odd rounds, keeping g mod 8. Mirrored rounds pair
   // long and short causal tiles, so the workgroups get equal work.
-  constexpr bool PERSIST = !VDMA;
+  constexpr bool PERSIST = D == 64;
   const int G = gridDim.x, g = blockIdx.x;
   auto item_of = [&](int round) -> int {
     const int off = (round & 1) ? ((G & 7) == 0 ? G - 8 * (1 + g / 8) + (g & 7) : G - 1 - g) : g;
@@ -618,8 +621,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
       n_kv = n_t;
     }
     load_q(cur);
-    // the first tiles' loads (positions 0 .. 2, and at D = 64 group 1's K of
-    // position 3); selects rather than a branch on the kind of walk
+    // the first tiles' loads (positions 0 .. 2, and without VDMA group 1's K
+    // of position 3); selects rather than a branch on the kind of walk
     if (PADMASK) ringv = ring_load(0);
     auto first_tile = [&](int k) -> int {
       return (PADMASK && use_list) ? __builtin_amdgcn_readlane(ringv, k) : toff + k;
@@ -655,8 +658,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(FwdParams p) {
     mbyte = 1u;
 
     // ---- ping-pong schedule: n_kv + 2 intervals, each closed by a workgroup
-    // barrier. M(t) = [PV(t-1), QK(t)] issues matrix-core work (and, at
-    // D = 64, the register staging of K and V), V(t) = [VDMA: K and V
+    // barrier. M(t) = [PV(t-1), QK(t)] issues matrix-core work (and, without
+    // VDMA, the register staging of K and V), V(t) = [VDMA: K and V
     // staging; softmax of S(t)] vector-ALU work. Interval 0:
     // group 0 runs QK(0). Interval t + 1 (t < n_kv): group 0 runs V(t) then
     // M(t + 1), group 1 runs M(t) then V(t) (M(n_kv) is PV(n_kv - 1) alone).
