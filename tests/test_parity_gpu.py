@@ -43,6 +43,7 @@ EDGE_CASES = {
     # more items than CUs, a partial last round, heads not a multiple of 8
     "rounds_causal_d64": (18, 3, 37, 600, 600, 64, dict(causal=True)),
     "rounds_lengths_d64": (19, 6, 16, 700, 650, 64, dict(mask="lengths")),
+    "rounds_dense_d64": (28, 3, 37, 600, 650, 64, {}),
     # whole 64-key tiles of padding inside the sequence (tiles 8 .. 23 and a
     # ragged block near the end): those tiles are not walked
     "interior_padding_causal_d128": (22, 2, 2, 700, 3000, 128, dict(mask="blocks", causal=True)),
