@@ -79,15 +79,16 @@ def code_sha256(path: str) -> str:
 MEASURED_TRAFFIC = {
     "B=1,H=32,s=8192,d=128,causal": {
         "code_sha256": "c0082fdb6527b4d7105219e1931b1a969d364d0030029b3c5c8dadf104c03397",
-        "fetch_bytes": 475422315,
+        "fetch_bytes": 479501646,
         "write_bytes": 68157440,
-        # SQ counter passes of the same command, on earlier sources with the same
-        # code for this kernel (mean over the launches after the first): MFMA-busy cycles per SIMD over SQ busy cycles per shader
+        # SQ counter passes of the same command (mean over the launches after
+        # the first; for the padded d=64 workload on an earlier source with
+        # the same code for that kernel): MFMA-busy cycles per SIMD over SQ busy cycles per shader
         # engine (32 engines), the clock those busy cycles imply over the
         # launch, LDS bank conflicts, LDS instructions per wave and 64-key tile
         "counters": {
-            "mfma_busy_frac": 0.689,
-            "sustained_clock_ghz": 1.70,
+            "mfma_busy_frac": 0.688,
+            "sustained_clock_ghz": 1.68,
             "lds_bank_conflicts": 0,
             "lds_instructions_per_wave_tile": 48,
         },
